@@ -1,0 +1,197 @@
+/*
+ * pda.h -- C ABI of the gfx950 paged-attention decode library (libpda.so).
+ *
+ * The operation (page "vLLM's custom ROCm paged-attention kernel wins all
+ * sixty cells", section 1 "What is being measured"; page "Hybrid-SSM decode
+ * rate on dual Radeon cards", the split-KV passage): pure decode, one query
+ * token per sequence attending over that sequence's whole cached context,
+ * where the context's K and V rows live in a block-paged cache addressed
+ * through a per-sequence block table, with grouped-query attention (G = Hq/Hkv
+ * query heads share one KV head).  For sequence b and query head h, with
+ * L = seq_lens[b] and g = floor(h / G):
+ *
+ *     out[b,h,:] = softmax_t( scale * q[b,h,:] . K[b,g,t,:] ) @ V[b,g,t,:]
+ *
+ * over t in [0, L), where row t of sequence b lives in physical block
+ * block_table[b][t / block_size] at slot t % block_size.  Slots at or past L
+ * in the final block (the "unwritten tail" the first page's section 5 and
+ * Figure 4 are about) never influence the output, whatever they hold: the
+ * score of such a slot is excluded by a select, and its V row is never read.
+ * The context of one (sequence, KV head) is split over P partitions of
+ * T_p tokens (the split-KV decode of the second page), each partition yields
+ * a partial (o, m, l), and a log-sum-exp merge combines them.
+ *
+ * Conventions for every entry point below:
+ *  - All array arguments of paged_decode_attn* are DEVICE pointers on the
+ *    current HIP device; shape and plan structs are HOST pointers.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no pointer after returning and has no global state except a
+ *    per-device cache of the compute-unit count.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No entry point synchronises the device, so a call can be
+ *    captured into a HIP graph.
+ *  - The return value is a status from host-side validation (PDA_OK or a
+ *    negative PDA_ERR_*).  On an error nothing is launched.
+ *
+ * Device-data contract (not checked on the hot path; violating it is
+ * undefined behaviour):
+ *  - 0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size;
+ *  - block_table[b][j] is in [0, num_blocks) for j < ceil(seq_lens[b] / block_size);
+ *    entries at or past that index are never read;
+ *  - K/V slots at or past seq_lens[b] may hold anything (NaN, Inf, garbage);
+ *  - seq_lens[b] == 0 yields a zero output row.
+ */
+#ifndef PDA_H
+#define PDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PDA_OK                0
+#define PDA_ERR_INVALID      -1  /* null pointer, non-positive size, Hq % Hkv != 0, bad plan */
+#define PDA_ERR_UNSUPPORTED  -2  /* head size not 64/128/256, G > PDA_MAX_GROUP, bad dtype */
+#define PDA_ERR_WORKSPACE    -3  /* workspace_bytes smaller than the plan needs */
+#define PDA_ERR_LAUNCH       -4  /* a kernel launch failed (hipGetLastError) */
+#define PDA_ERR_DEVICE       -5  /* the HIP device query failed */
+
+/* ---- element types ----------------------------------------------------- */
+/* q, k_cache, v_cache and out share one 16-bit type; arithmetic is fp32 and
+ * the output is rounded to nearest-even. */
+#define PDA_BF16 0
+#define PDA_FP16 1
+
+/* Largest supported query-to-KV head ratio G. */
+#define PDA_MAX_GROUP 16
+
+/* ---- kernel variants --------------------------------------------------- */
+/* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
+ *   with per-lane fp32 FMAs.
+ * PDA_VARIANT_MFMA: QK^T and PV on 16x16x32 matrix-core tiles (the packed
+ *   query group is padded to 16 rows).
+ * The plan picks VALU for G <= PDA_VALU_MAX_GROUP and MFMA above it. */
+#define PDA_VARIANT_VALU 1
+#define PDA_VARIANT_MFMA 2
+#define PDA_VALU_MAX_GROUP 16
+
+/* ---- the partition plan -------------------------------------------------
+ * A pure integer function of (num_seqs B, num_kv_heads Hkv, head_size D,
+ * max_seq_len Lmax, cu_count C).  With
+ *   PDA_TILE          16   tokens per wavefront tile
+ *   PDA_WAVES          4   wavefronts per workgroup
+ *   PDA_TP_ALIGN      64   = PDA_TILE * PDA_WAVES, granularity of T_p
+ *   PDA_WG_PER_CU      2   target number of workgroups per compute unit
+ *   PDA_WG_MIN_BYTES  64 KiB and PDA_WG_MAX_BYTES 512 KiB of K+V per workgroup
+ *   bpt   = 4 * D                            (K and V bytes per token, one KV head)
+ *   T_min = max(ALIGN, floor(MIN_BYTES / bpt / ALIGN) * ALIGN)
+ *   T_max = max(T_min, floor(MAX_BYTES / bpt / ALIGN) * ALIGN)
+ *   units = B * Hkv
+ *   P_tgt = ceil(WG_PER_CU * C / units)
+ *   T_p   = clamp(roundup(ceil(Lmax / P_tgt), ALIGN), T_min, T_max)
+ *   P     = max(1, ceil(Lmax / T_p))
+ * Partition p of (b, g) covers tokens [p*T_p, min((p+1)*T_p, seq_lens[b]));
+ * it is empty when p*T_p >= seq_lens[b].  The grid of the main kernel is
+ * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
+ * workspace is used; otherwise it writes fp32 partials and a merge kernel
+ * combines them, and the workspace holds
+ *   partial outputs  [B][Hq][P][D] fp32, then (m, l) pairs [B][Hq][P][2] fp32,
+ * each part aligned to 256 bytes. */
+#define PDA_TILE          16
+#define PDA_WAVES         4
+#define PDA_TP_ALIGN      64
+#define PDA_WG_PER_CU     2
+#define PDA_WG_MIN_BYTES  (64 * 1024)
+#define PDA_WG_MAX_BYTES  (512 * 1024)
+
+typedef struct pda_shape {
+    int32_t num_seqs;            /* B >= 1 */
+    int32_t num_q_heads;         /* Hq >= 1, multiple of num_kv_heads */
+    int32_t num_kv_heads;        /* Hkv >= 1 */
+    int32_t head_size;           /* D: 64, 128 or 256 */
+    int32_t block_size;          /* bs >= 1 (any value, e.g. 16 or 784) */
+    int32_t num_blocks;          /* NB >= 1: blocks in each of k_cache, v_cache */
+    int32_t max_blocks_per_seq;  /* MBS >= 1: row length of block_table */
+    int32_t max_seq_len;         /* >= every seq_lens[b], <= MBS * bs; sizes the plan */
+    int32_t dtype;               /* PDA_BF16 or PDA_FP16 */
+} pda_shape_t;
+
+typedef struct pda_plan {
+    int32_t num_partitions;        /* P >= 1 */
+    int32_t tokens_per_partition;  /* T_p, a positive multiple of PDA_TP_ALIGN */
+    int32_t variant;               /* PDA_VARIANT_VALU or PDA_VARIANT_MFMA */
+    int32_t cu_count;              /* the C the plan was made for */
+    int64_t workspace_bytes;       /* 0 when P == 1 */
+} pda_plan_t;
+
+/* Validate a shape: PDA_OK, PDA_ERR_INVALID or PDA_ERR_UNSUPPORTED.  Pure. */
+int pda_check_shape(const pda_shape_t* shape);
+
+/* The plan above for an explicit compute-unit count.  Pure and host-only:
+ * it needs no GPU.  Writes *plan and returns PDA_OK, or an error status. */
+int pda_plan_for_cus(const pda_shape_t* shape, int32_t cu_count, pda_plan_t* plan);
+
+/* The plan for the current HIP device (its compute-unit count is queried
+ * once per device and cached).  Returns PDA_ERR_DEVICE if the query fails. */
+int paged_decode_attn_plan(const pda_shape_t* shape, pda_plan_t* plan);
+
+/* Workspace bytes paged_decode_attn needs on the current device (0 when the
+ * plan has a single partition).  Returns a negative status on error. */
+int64_t paged_decode_attn_workspace_size(const pda_shape_t* shape);
+
+/* Workspace bytes a given plan needs (0 when plan->num_partitions == 1). */
+int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
+
+/* The decode step.
+ *   q            [B][Hq][D]           16-bit, the one query token per sequence
+ *   k_cache      [NB][Hkv][bs][D]     16-bit, the paged K pool
+ *   v_cache      [NB][Hkv][bs][D]     16-bit, the paged V pool (same layout)
+ *   block_table  [B][MBS]             int32 physical block ids, row-major
+ *   seq_lens     [B]                  int32 context lengths
+ *   scale        multiplies q.k before the softmax (usually 1/sqrt(D))
+ *   out          [B][Hq][D]           16-bit, written in full
+ *   workspace    device scratch of workspace_bytes (may be NULL if the plan
+ *                needs none); its contents on entry do not matter
+ * Returns PDA_OK once the kernels are enqueued on `stream`. */
+int paged_decode_attn(const pda_shape_t* shape,
+                      const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, void* out,
+                      void* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/* The same step under a caller-chosen plan (a partition count and size that
+ * cover max_seq_len, and a variant).  Tests use it to force P == 1 or a
+ * variant; results differ from the planned call only by fp32 rounding order. */
+int paged_decode_attn_with_plan(const pda_shape_t* shape, const pda_plan_t* plan,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                float scale, void* out,
+                                void* workspace, int64_t workspace_bytes,
+                                void* stream);
+
+/* Bookkeeping trace.  Runs the main kernel's own partitioning, tiling and
+ * address generation (the same device functions) under `plan`, but instead of
+ * loading K/V it records, for every token t the kernel consumes:
+ *   trace_slot [B][Hkv][max_seq_len]  physical slot  block_id * bs + (t % bs)
+ *   trace_part [B][Hkv][max_seq_len]  the partition p that consumed t
+ * and for every unit trace_range [B][Hkv][P][2] = (t0, t1) (t1 <= t0 when the
+ * partition is empty).  Entries for t >= seq_lens[b] are left untouched.
+ * Device pointers; the caller pre-fills them with a sentinel. */
+int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t* trace_slot, int32_t* trace_part,
+                            int32_t* trace_range, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* pda_status_string(int status);
+
+/* Build identification: library version, target and compile flags. */
+const char* pda_build_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PDA_H */

@@ -1,0 +1,161 @@
+"""CPU oracle for single-token paged-attention decode.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke entry
+point (``__graft_entry__.smoke``) and the CPU-baseline leg of ``bench.py`` may
+import it.  It shares no code with the GPU library (``paged_kv_cache_decode_amd``)
+and never imports it; the GPU library never imports this package.
+
+Contents
+  decode / decode_rows / partial   fp32 two-pass softmax(q K^T * scale) V over
+                                   the contiguous, pre-paging K/V tensors
+                                   (oracle.c, via ctypes).  The pages fix the
+                                   reference at fp32 computed from pre-paging
+                                   KV (page "vLLM's custom ROCm paged-attention
+                                   kernel wins all sixty cells", section 1).
+  plan                             the partition plan, re-derived from its
+                                   documentation in include/pda.h (plan.py).
+  bookkeeping                      expected per-token physical slot and
+                                   partition, and per-unit token ranges
+                                   (bookkeeping.py).
+  rel_linf                         the pages' score: relative L-infinity
+                                   against the reference's own scale.
+
+Inputs to decode*: ``q`` float32 [B, Hq, D]; ``k`` and ``v`` lists over b of
+float32 [Hkv, L_b, D] (exact upcasts of the 16-bit data).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import plan  # noqa: F401  (re-export)
+from . import bookkeeping  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from .build import build_oracle
+        build_oracle()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.oracle_decode_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, ctypes.c_float,
+                                       i32, P, P, P, i32]
+    lib.oracle_decode_rows.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [i32, i32, i32, i32, P, P, P, P, P, ctypes.c_float, P, i32]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_partial.argtypes = [i32, i32, i32, i32, P, P, P, P, P, ctypes.c_float,
+                                   i32, i32, i32, i32, P, P, P]
+    lib.oracle_partial.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class _Packed:
+    """Concatenates per-sequence [Hkv, L_b, D] tensors into one buffer."""
+
+    def __init__(self, q, k, v, seq_lens):
+        self.q = np.ascontiguousarray(q, dtype=np.float32)
+        B, Hq, D = self.q.shape
+        self.B, self.Hq, self.D = B, Hq, D
+        self.seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        assert self.seq_lens.shape == (B,)
+        assert len(k) == B and len(v) == B
+        Hkv = k[0].shape[0]
+        self.Hkv = Hkv
+        sizes = []
+        for b in range(B):
+            L = int(self.seq_lens[b])
+            assert k[b].shape == (Hkv, L, D), (k[b].shape, (Hkv, L, D))
+            assert v[b].shape == (Hkv, L, D)
+            sizes.append(Hkv * L * D)
+        self.kv_off = np.zeros(B, dtype=np.int64)
+        if B > 1:
+            self.kv_off[1:] = np.cumsum(sizes[:-1])
+        total = max(1, int(sum(sizes)))
+        self.k = np.empty(total, dtype=np.float32)
+        self.v = np.empty(total, dtype=np.float32)
+        for b in range(B):
+            o, n = int(self.kv_off[b]), sizes[b]
+            self.k[o:o + n] = np.asarray(k[b], dtype=np.float32).reshape(-1)
+            self.v[o:o + n] = np.asarray(v[b], dtype=np.float32).reshape(-1)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def decode(q, k, v, seq_lens, scale, nthreads: int = 0) -> np.ndarray:
+    """All rows: float32 [B, Hq, D]."""
+    lib = _load()
+    pk = _Packed(q, k, v, seq_lens)
+    out = np.empty((pk.B, pk.Hq, pk.D), dtype=np.float32)
+    rc = lib.oracle_decode(pk.B, pk.Hq, pk.Hkv, pk.D, _ptr(pk.seq_lens), _ptr(pk.kv_off),
+                           _ptr(pk.q), _ptr(pk.k), _ptr(pk.v), float(scale), _ptr(out),
+                           int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_decode failed")
+    return out
+
+
+def decode_rows(q, k, v, seq_lens, scale, rows, nthreads: int = 0) -> np.ndarray:
+    """Selected (b, h) rows: float32 [len(rows), D]."""
+    lib = _load()
+    pk = _Packed(q, k, v, seq_lens)
+    rows = list(rows)
+    rb = np.ascontiguousarray([r[0] for r in rows], dtype=np.int32)
+    rh = np.ascontiguousarray([r[1] for r in rows], dtype=np.int32)
+    out = np.empty((len(rows), pk.D), dtype=np.float32)
+    rc = lib.oracle_decode_rows(pk.B, pk.Hq, pk.Hkv, pk.D, _ptr(pk.seq_lens), _ptr(pk.kv_off),
+                                _ptr(pk.q), _ptr(pk.k), _ptr(pk.v), float(scale), len(rows),
+                                _ptr(rb), _ptr(rh), _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_decode_rows failed")
+    return out
+
+
+def partial(q, k, v, seq_lens, scale, b, h, t0, t1):
+    """Two-pass softmax over tokens [t0, t1) of row (b, h): (o[D], m, l),
+    natural-exp domain, o normalised by l."""
+    lib = _load()
+    pk = _Packed(q, k, v, seq_lens)
+    o = np.empty(pk.D, dtype=np.float32)
+    m = np.zeros(1, dtype=np.float32)
+    l = np.zeros(1, dtype=np.float32)
+    rc = lib.oracle_partial(pk.B, pk.Hq, pk.Hkv, pk.D, _ptr(pk.seq_lens), _ptr(pk.kv_off),
+                            _ptr(pk.q), _ptr(pk.k), _ptr(pk.v), float(scale), int(b), int(h),
+                            int(t0), int(t1), _ptr(o), _ptr(m), _ptr(l))
+    if rc != 0:
+        raise ValueError("oracle_partial failed")
+    return o, float(m[0]), float(l[0])
+
+
+def rel_linf(got, ref) -> float:
+    """max |got - ref| / max |ref| -- relative L-infinity against the
+    reference's own scale (page "vLLM's custom ROCm paged-attention kernel
+    wins all sixty cells", section 1).  A NaN anywhere in ``got`` gives inf;
+    an all-zero reference compares absolutely."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"shape mismatch {got.shape} vs {ref.shape}")
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)))
+    return err / scale if scale > 0 else err

@@ -1,0 +1,58 @@
+"""Partition plan, re-derived from its documentation in include/pda.h.
+
+TEST INFRASTRUCTURE.  This is an independent re-implementation, written from
+the formula stated in the header's comment, not from the library's C++; the
+tests require the library's plan to equal this one bit for bit.
+
+The pages do not print the split heuristic of the split-KV decode they
+measure (page "Hybrid-SSM decode rate on dual Radeon cards", split-KV
+passage: the KV range is split over more workgroups and reduced afterwards),
+so the rule is this library's own; what the pages fix is the reason for it:
+4 KV heads at batch 1 leave too little to spread over the compute units
+(same page, the occupancy table and the paragraph under it).
+"""
+
+TILE = 16
+WAVES = 4
+TP_ALIGN = TILE * WAVES
+WG_PER_CU = 2
+WG_MIN_BYTES = 64 * 1024
+WG_MAX_BYTES = 512 * 1024
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def token_bounds(head_size: int):
+    """(T_min, T_max) in tokens for one workgroup."""
+    bpt = 4 * head_size  # K and V, 16-bit, one KV head
+    t_min = max(TP_ALIGN, (WG_MIN_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
+    t_max = max(t_min, (WG_MAX_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
+    return t_min, t_max
+
+
+def partition(num_seqs: int, num_kv_heads: int, head_size: int, max_seq_len: int,
+              cu_count: int):
+    """(P, T_p) for the documented rule."""
+    t_min, t_max = token_bounds(head_size)
+    units = num_seqs * num_kv_heads
+    p_tgt = _cdiv(WG_PER_CU * cu_count, units)
+    if max_seq_len <= 0:
+        t_p = t_min
+    else:
+        t_p = _cdiv(_cdiv(max_seq_len, p_tgt), TP_ALIGN) * TP_ALIGN
+        t_p = min(max(t_p, t_min), t_max)
+    p = max(1, _cdiv(max_seq_len, t_p))
+    return p, t_p
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int) -> int:
+    """Partial outputs [B][Hq][P][D] fp32 then (m, l) [B][Hq][P][2] fp32, each
+    part rounded up to 256 bytes; none when P == 1."""
+    if p <= 1:
+        return 0
+
+    def r256(x):
+        return _cdiv(x, 256) * 256
+    return r256(num_seqs * num_q_heads * p * head_size * 4) + r256(num_seqs * num_q_heads * p * 2 * 4)

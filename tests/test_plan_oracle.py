@@ -1,0 +1,63 @@
+"""Pins of the bookkeeping oracle: the partition plan against hand-derived
+values and its invariants, and the expected trace against a brute-force loop
+over tokens.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import kvgen
+from oracle import bookkeeping, plan
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "plan_cu256.json")
+
+
+def test_plan_hand_derived_values():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        P, T = plan.partition(c["B"], c["Hkv"], c["D"], c["Lmax"], g["cu_count"])
+        assert (P, T) == (c["P"], c["T_p"]), c["name"]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_plan_invariants(D):
+    rng = np.random.default_rng(D)
+    t_min, t_max = plan.token_bounds(D)
+    for _ in range(2000):
+        B = int(rng.integers(1, 129))
+        Hkv = int(rng.integers(1, 33))
+        L = int(rng.integers(0, 200000))
+        cu = int(rng.choice([1, 80, 104, 256, 304]))
+        P, T = plan.partition(B, Hkv, D, L, cu)
+        assert T % plan.TP_ALIGN == 0 and t_min <= T <= t_max
+        assert P >= 1 and P * T >= L
+        if L > 0:
+            assert (P - 1) * T < L          # no partition is empty at Lmax
+        else:
+            assert P == 1
+
+
+def test_workspace_bytes():
+    assert plan.workspace_bytes(1, 32, 128, 1) == 0
+    assert plan.workspace_bytes(1, 24, 256, 128) == 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4
+
+
+def test_expected_trace_matches_token_loop():
+    case = kvgen.make_case(3, 8, 2, 64, 5, [0, 23, 61], seed=43, extra_blocks=2)
+    P, T = 2, 64  # partitions of 64 tokens, 2 of them cover Lmax=61
+    slot, part, ranges, valid = bookkeeping.expected_trace(
+        case.block_table.numpy(), case.seq_lens, 2, case.bs, 64, P, T)
+    table = case.block_table.numpy()
+    for b in range(3):
+        L = case.seq_lens[b]
+        for g in range(2):
+            for t in range(64):
+                assert valid[b, g, t] == (t < L)
+                if t < L:
+                    assert slot[b, g, t] == table[b][t // 5] * 5 + t % 5
+                    assert part[b, g, t] == t // T
+            for p in range(P):
+                t0, t1 = ranges[b, g, p]
+                assert t0 == p * T and t1 == min(p * T + T, L)
