@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+Headline workload (one "step" = one decode call = split-KV kernel + merge
+kernel): the pages' shape sweep at its longest context -- batch 1, 32 query
+heads over 8 KV heads (ratio 4), head size 128, block size 16, 32768 cached
+tokens, bf16 KV ~ N(0,1), zero-filled pool, randomly permuted block table.
+
+Metric: achieved HBM bandwidth over the algorithmic KV bytes (valid tokens
+only, K and V, 16-bit: L * Hkv * D * 2 * 2 bytes per call) as GB/s and as a
+fraction of the 8 TB/s peak, plus microseconds per call.
+
+Inputs are resident in HBM before timing starts.  Because one call's KV
+(128 MiB) would fit in the 256 MB Infinity Cache, consecutive calls rotate
+over enough replica pools (same content, same table) that no call finds its
+KV in a cache.  Device time comes from HIP events on the stream the kernels
+run on; the split-KV kernel's own duration from events the library attaches
+to that launch (hipExtLaunchKernel).
+
+Prints ONE JSON line.  Options: --gpus (1 only), --steps, --warmup,
+--cpu-seconds (oracle baseline budget), --no-extra (skip the other shapes).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 2 << 30     # >= 2 GiB of distinct KV between reuses of one pool
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def replicas_for(case):
+    import torch
+    pool = case.k_cache.numel() * case.k_cache.element_size() * 2
+    n = max(1, math.ceil(ROTATE_BYTES / pool))
+    reps = [(case.k_cache, case.v_cache)]
+    for _ in range(n - 1):
+        reps.append((case.k_cache.clone(), case.v_cache.clone()))
+    torch.cuda.synchronize()
+    return reps
+
+
+def time_case(case, steps, warmup, passes=1):
+    """Returns dict with per-call device time, split-KV kernel time, plan."""
+    import torch
+    import paged_kv_cache_decode_amd as pda
+    shape = pda.make_shape(case.B, case.Hq, case.Hkv, case.D, case.bs, case.num_blocks,
+                           case.max_blocks_per_seq, case.max_seq_len, case.dtype)
+    plan = pda.paged_decode_attn_plan(shape)
+    out = torch.empty_like(case.q)
+    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=case.q.device)
+    reps = replicas_for(case)
+    R = len(reps)
+
+    def call(i, e0=None, e1=None):
+        kc, vc = reps[i % R]
+        pda.paged_decode_attn_timed(shape, plan, case.q, kc, vc, case.block_table,
+                                    case.seq_lens_t, case.scale, out, ws, e0, e1)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for e in ev0 + ev1:
+        e.record()  # materialise the HIP event before the library uses it
+    torch.cuda.synchronize()
+    results = []
+    for _ in range(passes):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            call(i, ev0[i], ev1[i])
+        stop.record()
+        torch.cuda.synchronize()
+        w1 = time.perf_counter()
+        call_ms = start.elapsed_time(stop) / steps
+        kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / steps
+        results.append(dict(call_ms=call_ms, kernel_ms=kern_ms, wall_ms=(w1 - w0) * 1e3 / steps))
+    best = min(results, key=lambda r: r["call_ms"])
+    med = sorted(results, key=lambda r: r["call_ms"])[len(results) // 2]
+    kv = case.kv_bytes()
+    return dict(out=out, plan=plan, replicas=R, passes=results, call_ms=med["call_ms"],
+                kernel_ms=med["kernel_ms"], wall_ms=med["wall_ms"], best_call_ms=best["call_ms"],
+                kv_bytes=kv)
+
+
+def summary(name, case, r):
+    us = r["call_ms"] * 1e3
+    kus = r["kernel_ms"] * 1e3
+    gbs = r["kv_bytes"] / (r["call_ms"] * 1e-3) / 1e9
+    kgbs = r["kv_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    return {"workload": name, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv, "D": case.D,
+            "block_size": case.bs, "dtype": case.dtype, "context_tokens": sum(case.seq_lens),
+            "kv_bytes": r["kv_bytes"], "P": r["plan"].num_partitions,
+            "T_p": r["plan"].tokens_per_partition, "us_per_call": round(us, 3),
+            "splitkv_kernel_us": round(kus, 3), "GBps": round(gbs, 1),
+            "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+            "kernel_GBps": round(kgbs, 1), "kernel_pct_of_peak": round(100 * kgbs / PEAK_GBS, 2),
+            "us_per_context_token": round(us / sum(case.seq_lens), 6),
+            "replica_pools": r["replicas"],
+            "passes_us": [round(p["call_ms"] * 1e3, 3) for p in r["passes"]]}
+
+
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, on the host cores, over the same workload."""
+    import oracle
+    import kvgen
+    q, k, v, lens = kvgen.oracle_inputs(case)
+    threads = oracle.num_threads()
+    n, t = 0, 0.0
+    ref = None
+    while t < seconds or n == 0:
+        t0 = time.perf_counter()
+        ref = oracle.decode(q, k, v, lens, case.scale, nthreads=threads)
+        t += time.perf_counter() - t0
+        n += 1
+    per_call = t / n
+    return ref, {"value": round(case.kv_bytes() / per_call / 1e9, 3), "unit": "GB/s",
+                 "cores": threads, "kind": "oracle",
+                 "us_per_call": round(per_call * 1e6, 1),
+                 "sample": f"{n} full decode call(s) of the headline workload "
+                           f"({case.B}x{case.Hq} rows over {sum(case.seq_lens)} tokens), "
+                           f"{t:.1f} s of CPU time, OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--passes", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path has no cross-GPU step to measure here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import oracle
+    import paged_kv_cache_decode_amd as pda
+    from kvgen import configs
+
+    torch.cuda.set_device(0)
+    pda.load_library()
+    log(f"library: {pda.pda_build_id()}")
+
+    L = 32768
+    case = configs.cfg2(32, L, device="cuda")
+    log("timing headline workload (cfg2 Hq 32 / Hkv 8, 32K)")
+    r = time_case(case, args.steps, args.warmup, passes=args.passes)
+    head = summary("paged_decode bf16 B1 Hq32 Hkv8 D128 bs16 L32768", case, r)
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        ref, cpu = cpu_baseline(case, args.cpu_seconds)
+        parity = oracle.rel_linf(r["out"].float().cpu().numpy(), ref)
+
+    extra = {}
+    if not args.no_extra:
+        small_steps = max(20, args.steps // 4)
+        specs = [(f"cfg2 Hq{hq} 32K", lambda hq=hq: configs.cfg2(hq, L, device="cuda"))
+                 for hq in (8, 16, 24)]
+        specs += [("cfg3 B1 bf16 32K", lambda: configs.cfg3(1, L, device="cuda")),
+                  ("cfg3 B1 fp16 32K", lambda: configs.cfg3(1, L, dtype="fp16", device="cuda")),
+                  ("cfg3 B8 bf16 32K", lambda: configs.cfg3(8, L, device="cuda"))]
+        specs += [(f"cfg4 {n}", lambda n=n: configs.cfg4(n, device="cuda"))
+                  for n in configs.CFG4_LENS]
+        specs += [("cfg5 B64 mixed", lambda: configs.cfg5(device="cuda"))]
+        for name, mk in specs:
+            log(f"timing {name}")
+            c = mk()
+            rr = time_case(c, small_steps, max(5, args.warmup // 4), passes=3)
+            extra[name] = summary(name, c, rr)
+            del c, rr
+            torch.cuda.empty_cache()
+        ladder = [(extra[f"cfg4 {n}"]["context_tokens"], extra[f"cfg4 {n}"]["us_per_call"])
+                  for n in configs.CFG4_LENS]
+        xs = np.array([a for a, _ in ladder], dtype=np.float64)
+        ys = np.array([b for _, b in ladder], dtype=np.float64)
+        slope = float(np.polyfit(xs, ys, 1)[0])
+        extra["cfg4 slope us per context token"] = round(slope, 6)
+
+    kbytes = r["kv_bytes"]
+    achieved = kbytes / (r["kernel_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "achieved KV HBM GB/s (% of MI355X peak) and us/call at 32K-context decode",
+        "value": head["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["call_ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "paged GQA decode, batch 1, 32 query / 8 KV heads, head 128, "
+                               "block 16, 32768-token context, bf16 KV ~N(0,1), permuted table",
+                   "global_batch": 1, "seq_len": L, "parallelism": "single GPU"},
+        "us_per_call": head["us_per_call"],
+        "pct_of_peak": head["pct_of_peak"],
+        "us_per_context_token": head["us_per_context_token"],
+        "plan": {"P": head["P"], "T_p": head["T_p"], "replica_pools": head["replica_pools"]},
+        "passes_us": head["passes_us"],
+        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel (split-KV)",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "kernel_us": round(r["kernel_ms"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": kbytes},
+        "cpu_baseline": cpu,
+        "parity_rel_linf_vs_oracle": parity,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

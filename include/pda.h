@@ -69,13 +69,14 @@ extern "C" {
 
 /* ---- kernel variants --------------------------------------------------- */
 /* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
- *   with per-lane fp32 FMAs.
- * PDA_VARIANT_MFMA: QK^T and PV on 16x16x32 matrix-core tiles (the packed
- *   query group is padded to 16 rows).
- * The plan picks VALU for G <= PDA_VALU_MAX_GROUP and MFMA above it. */
+ *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
+ * PDA_VARIANT_MFMA: QK^T and PV on matrix-core tiles, the packed query group
+ *   padded to 16 rows; reserved, not built in this version (a plan naming it
+ *   is rejected with PDA_ERR_UNSUPPORTED).
+ * The plan picks VALU. */
 #define PDA_VARIANT_VALU 1
 #define PDA_VARIANT_MFMA 2
-#define PDA_VALU_MAX_GROUP 16
+#define PDA_VALU_MAX_GROUP 8
 
 /* ---- the partition plan -------------------------------------------------
  * A pure integer function of (num_seqs B, num_kv_heads Hkv, head_size D,
@@ -171,6 +172,19 @@ int paged_decode_attn_with_plan(const pda_shape_t* shape, const pda_plan_t* plan
                                 float scale, void* out,
                                 void* workspace, int64_t workspace_bytes,
                                 void* stream);
+
+/* Instrumented decode step for benchmarks: identical to
+ * paged_decode_attn_with_plan (plan may be NULL for the device's own plan),
+ * but the split-KV kernel is launched with hipExtLaunchKernel so that the
+ * caller's events `start_event` / `stop_event` (hipEvent_t, created by the
+ * caller, may be NULL) record that kernel's own start and end on `stream`.
+ * The merge kernel, if any, follows on the same stream untimed. */
+int paged_decode_attn_timed(const pda_shape_t* shape, const pda_plan_t* plan,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            float scale, void* out,
+                            void* workspace, int64_t workspace_bytes,
+                            void* start_event, void* stop_event, void* stream);
 
 /* Bookkeeping trace.  Runs the main kernel's own partitioning, tiling and
  * address generation (the same device functions) under `plan`, but instead of

@@ -1,0 +1,270 @@
+"""Python binding of libpda.so, the gfx950 paged-attention decode library.
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  torch supplies device memory and the current stream; nothing else
+from torch touches the path.  The binding raises if libpda.so is missing --
+there is no CPU fallback.
+
+Names mirror the C ABI in include/pda.h:
+  paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale, out, ...)
+  paged_decode_attn_workspace_size(shape)
+  paged_decode_attn_plan(shape) / pda_plan_for_cus(shape, cu_count)
+  paged_decode_attn_with_plan(...) / paged_decode_attn_trace(...)
+  pda_status_string(status) / pda_build_id()
+"""
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpda.so")
+
+PDA_OK = 0
+PDA_ERR_INVALID = -1
+PDA_ERR_UNSUPPORTED = -2
+PDA_ERR_WORKSPACE = -3
+PDA_ERR_LAUNCH = -4
+PDA_ERR_DEVICE = -5
+PDA_BF16 = 0
+PDA_FP16 = 1
+PDA_VARIANT_VALU = 1
+PDA_VARIANT_MFMA = 2
+
+_DTYPES = {"bf16": PDA_BF16, "fp16": PDA_FP16}
+
+
+class PdaShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class PdaPlan(ctypes.Structure):
+    _fields_ = [("num_partitions", ctypes.c_int32), ("tokens_per_partition", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class PdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {pda_status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libpda.so (built in-tree by __graft_entry__.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    sp, pp = ctypes.POINTER(PdaShape), ctypes.POINTER(PdaPlan)
+    lib.pda_check_shape.argtypes = [sp]
+    lib.pda_check_shape.restype = ctypes.c_int
+    lib.pda_plan_for_cus.argtypes = [sp, ctypes.c_int32, pp]
+    lib.pda_plan_for_cus.restype = ctypes.c_int
+    lib.paged_decode_attn_plan.argtypes = [sp, pp]
+    lib.paged_decode_attn_plan.restype = ctypes.c_int
+    lib.paged_decode_attn_workspace_size.argtypes = [sp]
+    lib.paged_decode_attn_workspace_size.restype = ctypes.c_int64
+    lib.pda_workspace_bytes.argtypes = [sp, pp]
+    lib.pda_workspace_bytes.restype = ctypes.c_int64
+    lib.paged_decode_attn.argtypes = [sp, P, P, P, P, P, ctypes.c_float, P, P, ctypes.c_int64, P]
+    lib.paged_decode_attn.restype = ctypes.c_int
+    lib.paged_decode_attn_with_plan.argtypes = [sp, pp, P, P, P, P, P, ctypes.c_float, P, P,
+                                                ctypes.c_int64, P]
+    lib.paged_decode_attn_with_plan.restype = ctypes.c_int
+    lib.paged_decode_attn_timed.argtypes = [sp, pp, P, P, P, P, P, ctypes.c_float, P, P,
+                                            ctypes.c_int64, P, P, P]
+    lib.paged_decode_attn_timed.restype = ctypes.c_int
+    lib.paged_decode_attn_trace.argtypes = [sp, pp, P, P, P, P, P, P]
+    lib.paged_decode_attn_trace.restype = ctypes.c_int
+    lib.pda_status_string.argtypes = [ctypes.c_int]
+    lib.pda_status_string.restype = ctypes.c_char_p
+    lib.pda_build_id.argtypes = []
+    lib.pda_build_id.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def make_shape(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
+               max_blocks_per_seq, max_seq_len, dtype="bf16") -> PdaShape:
+    dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return PdaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_size),
+                    int(block_size), int(num_blocks), int(max_blocks_per_seq), int(max_seq_len),
+                    dt)
+
+
+def shape_from_tensors(q, k_cache, block_table, max_seq_len: int) -> PdaShape:
+    import torch
+    B, Hq, D = q.shape
+    NB, Hkv, bs, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head size of q and k_cache differ")
+    dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(q.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return make_shape(B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seq_len, dt)
+
+
+def pda_status_string(status: int) -> str:
+    return load_library().pda_status_string(int(status)).decode()
+
+
+def pda_build_id() -> str:
+    return load_library().pda_build_id().decode()
+
+
+def pda_check_shape(shape: PdaShape) -> int:
+    return int(load_library().pda_check_shape(ctypes.byref(shape)))
+
+
+def pda_plan_for_cus(shape: PdaShape, cu_count: int) -> PdaPlan:
+    plan = PdaPlan()
+    rc = load_library().pda_plan_for_cus(ctypes.byref(shape), int(cu_count), ctypes.byref(plan))
+    if rc != PDA_OK:
+        raise PdaError(rc, "pda_plan_for_cus")
+    return plan
+
+
+def paged_decode_attn_plan(shape: PdaShape) -> PdaPlan:
+    plan = PdaPlan()
+    rc = load_library().paged_decode_attn_plan(ctypes.byref(shape), ctypes.byref(plan))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_plan")
+    return plan
+
+
+def paged_decode_attn_workspace_size(shape: PdaShape) -> int:
+    n = int(load_library().paged_decode_attn_workspace_size(ctypes.byref(shape)))
+    if n < 0:
+        raise PdaError(n, "paged_decode_attn_workspace_size")
+    return n
+
+
+def pda_workspace_bytes(shape: PdaShape, plan: PdaPlan) -> int:
+    return int(load_library().pda_workspace_bytes(ctypes.byref(shape), ctypes.byref(plan)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype):
+        raise ValueError("q, k_cache, v_cache and out must share one dtype")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if seq_lens.shape != (q.shape[0],) or block_table.shape[0] != q.shape[0]:
+        raise ValueError("seq_lens / block_table do not match the batch")
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, out=None,
+                      workspace=None, max_seq_len: Optional[int] = None, plan: Optional[PdaPlan] = None,
+                      stream=None):
+    """Decode one query token per sequence over the paged KV cache.
+
+    q [B, Hq, D], k_cache/v_cache [NB, Hkv, bs, D] (bf16 or fp16, one dtype),
+    block_table [B, MBS] int32, seq_lens [B] int32, all on the current device.
+    max_seq_len must bound every seq_lens entry (default: block_table width *
+    block size, which is always valid but may over-partition).  Returns `out`.
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out)
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * k_cache.shape[2]
+    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len)
+    lib = load_library()
+    if plan is None:
+        need = paged_decode_attn_workspace_size(shape)
+    else:
+        need = pda_workspace_bytes(shape, plan)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if plan is None:
+        rc = lib.paged_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_table), _ptr(seq_lens), float(scale), _ptr(out),
+                                   _ptr(workspace), ws_bytes, _stream(stream))
+    else:
+        rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(plan), _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             _ptr(seq_lens), float(scale), _ptr(out),
+                                             _ptr(workspace), ws_bytes, _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn")
+    return out
+
+
+def paged_decode_attn_with_plan(q, k_cache, v_cache, block_table, seq_lens, scale: float,
+                                plan: PdaPlan, out=None, workspace=None,
+                                max_seq_len: Optional[int] = None, stream=None):
+    return paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale, out=out,
+                             workspace=workspace, max_seq_len=max_seq_len, plan=plan,
+                             stream=stream)
+
+
+def paged_decode_attn_timed(shape: PdaShape, plan: Optional[PdaPlan], q, k_cache, v_cache,
+                            block_table, seq_lens, scale: float, out, workspace,
+                            start_event=None, stop_event=None, stream=None):
+    """Low-level instrumented call for benchmarks: no argument conversion,
+    pre-allocated `out` / `workspace`; start_event / stop_event are
+    torch.cuda.Event objects (already recorded once, so they exist) that the
+    library attaches to the split-KV kernel's own start and end."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ev0 = None if start_event is None else start_event.cuda_event
+    ev1 = None if stop_event is None else stop_event.cuda_event
+    rc = load_library().paged_decode_attn_timed(
+        ctypes.byref(shape), None if plan is None else ctypes.byref(plan), _ptr(q),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), float(scale),
+        _ptr(out), _ptr(workspace), ws_bytes, ev0, ev1, _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_timed")
+
+
+def paged_decode_attn_trace(shape: PdaShape, plan: PdaPlan, block_table, seq_lens,
+                            stream=None, fill: int = -1):
+    """Run the bookkeeping trace; returns (slot [B,Hkv,Lmax], part [B,Hkv,Lmax],
+    ranges [B,Hkv,P,2]) as int32 device tensors pre-filled with `fill`."""
+    import torch
+    dev = block_table.device
+    B, Hkv, Lmax, P = shape.num_seqs, shape.num_kv_heads, shape.max_seq_len, plan.num_partitions
+    slot = torch.full((B, Hkv, max(Lmax, 1)), fill, dtype=torch.int32, device=dev)
+    part = torch.full_like(slot, fill)
+    ranges = torch.full((B, Hkv, P, 2), fill, dtype=torch.int32, device=dev)
+    rc = load_library().paged_decode_attn_trace(ctypes.byref(shape), ctypes.byref(plan),
+                                                _ptr(block_table), _ptr(seq_lens), _ptr(slot),
+                                                _ptr(part), _ptr(ranges), _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_trace")
+    return slot, part, ranges

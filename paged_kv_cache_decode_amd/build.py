@@ -1,0 +1,71 @@
+"""Build libpda.so in-tree with hipcc for gfx950 only.
+
+Every translation unit is compiled in parallel into _build/, then linked into
+paged_kv_cache_decode_amd/libpda.so.  The decode kernel's source is compiled
+once per (element type, head size).
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libpda.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+ARCH = "gfx950"
+# -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_fma_f32 and kin)
+CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _units():
+    units = []
+    for dt in (0, 1):
+        for hd in (64, 128, 256):
+            units.append((os.path.join(CSRC, "pda_decode_valu.hip"),
+                          f"valu_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
+    units.append((os.path.join(CSRC, "pda_merge.hip"), "merge.o", []))
+    units.append((os.path.join(CSRC, "pda_trace.hip"), "trace.o", []))
+    flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops"])
+    units.append((os.path.join(CSRC, "pda_host.cpp"), "host.o",
+                   ["-x", "hip", f'-DPDA_BUILD_FLAGS="{flags}"']))
+    return units
+
+
+def _compile(unit, verbose):
+    src, obj, extra = unit
+    out = os.path.join(BUILD, obj)
+    cmd = [HIPCC] + CFLAGS + extra + ["-c", src, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src} {extra}:\n{r.stderr}")
+    # the host pass does not know the device-only feature: harmless, filter it
+    warn = "\n".join(x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x)
+    if warn.strip() and verbose:
+        print(warn, file=sys.stderr)
+    return out
+
+
+def build_library(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    units = _units()
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, 16))) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), units))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

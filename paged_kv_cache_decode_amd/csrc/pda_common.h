@@ -1,0 +1,107 @@
+// Shared definitions of the gfx950 paged-decode library: kernel parameter
+// block, fast division by the (runtime) block size, and the launcher
+// declarations the host runtime calls.  Internal to libpda.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pda.h"
+
+namespace pda {
+
+// Unsigned division by a runtime constant d >= 1 for dividends n < 2^31,
+// by the round-up multiply-high method of Granlund and Montgomery
+// ("Division by invariant integers using multiplication", 1994):
+//   l = ceil(log2 d),  m = floor(2^32 * (2^l - d) / d) + 1,
+//   n / d = (mulhi(n, m) + n) >> l.
+// mulhi(n, m) < n, so the sum fits in 32 bits for n < 2^31.  Used to split a
+// token index into (logical block, slot) for any block size, including ones
+// that are not powers of two (784 = 16 x 49).
+struct FastDiv {
+    uint32_t d;
+    uint32_t mul;
+    uint32_t shift;
+};
+
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.shift = l;
+    f.mul = (uint32_t)((((1ull << l) - d) << 32) / d + 1ull);
+    return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t hi = __umulhi(n, f.mul);
+#else
+    uint32_t hi = (uint32_t)(((uint64_t)n * f.mul) >> 32);
+#endif
+    return (hi + n) >> f.shift;
+}
+
+// Everything one decode launch needs; passed by value as the kernel argument.
+struct DecodeParams {
+    const void* q;             // [B][Hq][D]
+    const void* k_cache;       // [NB][Hkv][bs][D]
+    const void* v_cache;       // [NB][Hkv][bs][D]
+    const int32_t* block_table;// [B][MBS]
+    const int32_t* seq_lens;   // [B]
+    void* out;                 // [B][Hq][D]
+    float* ws_o;               // [B][Hq][P][D]    (P > 1 only)
+    float* ws_ml;              // [B][Hq][P][2]    (P > 1 only)
+    int32_t* trace_slot;       // trace kernel only
+    int32_t* trace_part;
+    int32_t* trace_range;
+    float scale_log2;          // scale * log2(e): scores live in the exp2 domain
+    int32_t num_q_heads;       // Hq
+    int32_t num_kv_heads;      // Hkv
+    int32_t group;             // G = Hq / Hkv
+    int32_t block_size;        // bs
+    int32_t max_blocks_per_seq;// MBS
+    int32_t max_seq_len;       // host bound on seq_lens (also the trace row length)
+    int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
+    int32_t num_partitions;    // P
+    int32_t tokens_per_part;   // T_p
+    int32_t tbl_capacity;      // LDS entries reserved for the block-table slice
+    FastDiv bs_div;
+    int64_t block_stride;      // Hkv * bs * D elements
+    int32_t head_stride;       // bs * D elements
+};
+
+constexpr int kWave = 64;
+constexpr int kWaves = PDA_WAVES;
+constexpr int kTile = PDA_TILE;
+constexpr int kThreads = kWave * kWaves;
+
+// Launchers (one translation unit per element type and head size).
+// `aligned` selects the path for block sizes that are multiples of the tile.
+// start/stop: optional events bracketing the decode kernel (hipExtLaunchKernel)
+hipError_t launch_decode_valu(int dtype, int head_size, int group_pad, bool aligned,
+                              const DecodeParams& p, int batch, hipStream_t stream,
+                              hipEvent_t start, hipEvent_t stop);
+hipError_t launch_merge(int dtype, int head_size, const DecodeParams& p, int batch,
+                        hipStream_t stream);
+hipError_t launch_trace(int head_size, bool aligned, const DecodeParams& p, int batch,
+                        hipStream_t stream);
+
+// Padded group sizes the VALU kernel is compiled for.
+inline int valu_group_pad(int g) {
+    if (g <= 4) return g;
+    if (g <= 6) return 6;
+    if (g <= 8) return 8;
+    if (g <= 12) return 12;
+    return 16;
+}
+
+// Bytes of dynamic LDS the decode kernel uses for a block-table slice of
+// `tbl_capacity` entries plus the cross-wave merge of `gpad` heads.
+inline size_t decode_lds_bytes(int head_size, int gpad, int tbl_capacity) {
+    size_t merge = (size_t)kWaves * gpad * (head_size + 2) * sizeof(float);
+    return merge + (size_t)tbl_capacity * sizeof(int32_t);
+}
+
+}  // namespace pda

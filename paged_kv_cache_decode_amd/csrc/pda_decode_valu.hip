@@ -1,0 +1,275 @@
+// Paged-attention decode, VALU variant, for gfx950.
+//
+// One workgroup (4 wavefronts) per unit (partition p, KV head g, sequence b).
+// All G query heads of the KV group are packed in the unit, so every K/V
+// byte of the partition is read from HBM once.  Each lane loads 16 contiguous
+// bytes of a token row; a row spans D/8 lanes, so a wavefront load covers
+// whole rows and consecutive lanes touch consecutive addresses.
+//
+// Per tile and lane:
+//   QK^T   packed dot2 over the lane's 8 elements, then a DPP sum over the
+//          row's lanes -> one score per packed head;
+//   mask   scores of tokens at or past the partition end are replaced by -inf
+//          with a select (tail slots are not even addressed: see
+//          locate_token), so NaN or garbage there cannot reach a score;
+//   online softmax in the exp2 domain, per lane sub-stream, with a rescale
+//          only when some lane's running max grew;
+//   PV     fp32 FMAs of the lane's 8 V elements.
+// At the end the sub-streams of a wavefront and then the 4 wavefronts are
+// merged with the log-sum-exp rule, in a fixed order (run-to-run identical).
+// With one partition the unit writes the 16-bit output; otherwise it writes
+// the fp32 partial (o, m, l) that the merge kernel combines.
+//
+// This translation unit is compiled once per (element type, head size):
+// PDA_DTYPE (0 bf16, 1 fp16) and PDA_HEAD (64, 128, 256).
+#include <hip/hip_ext.h>
+
+#include "pda_device.h"
+
+#ifndef PDA_DTYPE
+#error "PDA_DTYPE must be defined"
+#endif
+#ifndef PDA_HEAD
+#error "PDA_HEAD must be defined"
+#endif
+
+namespace pda {
+
+// The element type and head size are template parameters of the kernel (not
+// only of this translation unit) so that every instantiation has its own
+// symbol name across the six translation units.
+template <typename Elt, int D, int GP, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+    using Geo = ValuGeom<D>;
+    constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U, TT = Geo::TT;
+    extern __shared__ float smem[];
+    float* red = smem;                                                  // [kWaves][GP][D+2]
+    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
+
+    const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int c = lane % LPT, r = lane / LPT;
+    const int G = p.group;
+    const int L = context_len(p, b);
+    const int t0 = part * p.tokens_per_part;
+    const bool direct = p.num_partitions == 1;
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+
+    if (t0 >= L) {  // empty partition; with one partition this is L == 0
+        if (direct)
+            for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+                out16[((int64_t)b * p.num_q_heads + g * G) * D + idx] = 0;
+        return;
+    }
+    const int t1 = min(t0 + p.tokens_per_part, L);
+    const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
+    const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
+    stage_table_slice(p, b, lb0, lb1, tbl);
+
+    // the packed query rows of this KV group: 8 elements per lane and head
+    uint4 qv[GP];
+    {
+        const uint16_t* qb = static_cast<const uint16_t*>(p.q) +
+                             ((int64_t)b * p.num_q_heads + g * G) * D + c * 8;
+#pragma unroll
+        for (int i = 0; i < GP; ++i)
+            qv[i] = (i < G) ? *reinterpret_cast<const uint4*>(qb + (int64_t)i * D)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache);
+    const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache);
+    const int64_t head_off = (int64_t)g * p.head_stride + c * 8;
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+
+    auto load_tile = [&](int j, uint4 (&kr)[U], uint4 (&vr)[U]) {
+        const int tile_base = t0 + j * TT;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int phys, slot;
+            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot);
+            const int64_t off = (int64_t)phys * p.block_stride + head_off + (int64_t)slot * D;
+            kr[u] = *reinterpret_cast<const uint4*>(kc + off);
+            vr[u] = *reinterpret_cast<const uint4*>(vc + off);
+        }
+    };
+
+    float m[GP], l[GP], acc[GP][8];
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+        m[i] = -FLT_MAX;  // finite floor: exp2(-inf - m) stays 0, never NaN
+        l[i] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    }
+
+    int j = wave;
+    uint4 kr[U], vr[U];
+    if (j < ntiles) load_tile(j, kr, vr);
+    for (; j < ntiles; j += kWaves) {
+        // prefetch the wave's next tile (the last iteration re-reads its own)
+        uint4 kn[U], vn[U];
+        load_tile(min(j + kWaves, ntiles - 1), kn, vn);
+
+        const int tile_base = t0 + j * TT;
+        const bool full = tile_base + TT <= t1;
+        float s[U][GP];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int i = 0; i < GP; ++i) {
+                float d = Elt::dot2(qv[i].x, kr[u].x, 0.f);
+                d = Elt::dot2(qv[i].y, kr[u].y, d);
+                d = Elt::dot2(qv[i].z, kr[u].z, d);
+                d = Elt::dot2(qv[i].w, kr[u].w, d);
+                s[u][i] = group_sum<LPT>(d) * p.scale_log2;
+            }
+        }
+        if (!full) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool valid = tile_base + u * R + r < t1;
+#pragma unroll
+                for (int i = 0; i < GP; ++i) s[u][i] = valid ? s[u][i] : -INFINITY;
+            }
+        }
+        bool grew = false;
+        float mn[GP];
+#pragma unroll
+        for (int i = 0; i < GP; ++i) {
+            float mt = s[0][i];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][i]);
+            mn[i] = fmaxf(m[i], mt);
+            grew |= mn[i] > m[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+            for (int i = 0; i < GP; ++i) {
+                const float alpha = exp2f(m[i] - mn[i]);
+                l[i] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[i][e] *= alpha;
+                m[i] = mn[i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            vf[0] = Elt::lo(vr[u].x); vf[1] = Elt::hi(vr[u].x);
+            vf[2] = Elt::lo(vr[u].y); vf[3] = Elt::hi(vr[u].y);
+            vf[4] = Elt::lo(vr[u].z); vf[5] = Elt::hi(vr[u].z);
+            vf[6] = Elt::lo(vr[u].w); vf[7] = Elt::hi(vr[u].w);
+#pragma unroll
+            for (int i = 0; i < GP; ++i) {
+                const float pw = exp2f(s[u][i] - m[i]);
+                l[i] += pw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(pw, vf[e], acc[i][e]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) { kr[u] = kn[u]; vr[u] = vn[u]; }
+    }
+
+    // merge the R lane sub-streams (lanes c, c+LPT, ...) of the wavefront
+#pragma unroll
+    for (int x = LPT; x < kWave; x <<= 1) {
+#pragma unroll
+        for (int i = 0; i < GP; ++i) {
+            const float mo = __shfl_xor(m[i], x);
+            const float lo = __shfl_xor(l[i], x);
+            const float mm = fmaxf(m[i], mo);
+            const float wa = exp2f(m[i] - mm), wb = exp2f(mo - mm);
+            l[i] = l[i] * wa + lo * wb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ao = __shfl_xor(acc[i][e], x);
+                acc[i][e] = acc[i][e] * wa + ao * wb;
+            }
+            m[i] = mm;
+        }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int i = 0; i < GP; ++i) {
+            float* row = red + (wave * GP + i) * (D + 2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) row[c * 8 + e] = acc[i][e];
+            if (c == 0) { row[D] = m[i]; row[D + 1] = l[i]; }
+        }
+    }
+    __syncthreads();
+
+    // merge the wavefronts and write the unit's result
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int i = idx / D, d = idx - i * D;
+        float M = -FLT_MAX;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * GP + i) * (D + 2) + D]);
+        float o = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float* row = red + (w * GP + i) * (D + 2);
+            const float wt = exp2f(row[D] - M);
+            den += row[D + 1] * wt;
+            o += row[d] * wt;
+        }
+        const int h = g * G + i;
+        if (direct) {
+            out16[((int64_t)b * p.num_q_heads + h) * D + d] = Elt::from_float(o / den);
+        } else {
+            const int64_t prow = ((int64_t)b * p.num_q_heads + h) * p.num_partitions + part;
+            p.ws_o[prow * D + d] = o / den;
+            if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
+        }
+    }
+}
+
+#if PDA_DTYPE == 0
+using EltT = BF16;
+#else
+using EltT = FP16;
+#endif
+constexpr int kHead = PDA_HEAD;
+
+template <int GP, bool ALIGNED>
+static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+    const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
+    const uint32_t lds = (uint32_t)decode_lds_bytes(kHead, GP, p.tbl_capacity);
+    if (start || stop)
+        hipExtLaunchKernelGGL((decode_valu_kernel<EltT, kHead, GP, ALIGNED>), grid, dim3(kThreads),
+                              lds, stream, start, stop, 0, p);
+    else
+        hipLaunchKernelGGL((decode_valu_kernel<EltT, kHead, GP, ALIGNED>), grid, dim3(kThreads),
+                           lds, stream, p);
+    return hipGetLastError();
+}
+
+template <bool ALIGNED>
+static hipError_t launch_gp(int gpad, const DecodeParams& p, int batch, hipStream_t s,
+                            hipEvent_t e0, hipEvent_t e1) {
+    switch (gpad) {
+        case 1: return launch_one<1, ALIGNED>(p, batch, s, e0, e1);
+        case 2: return launch_one<2, ALIGNED>(p, batch, s, e0, e1);
+        case 3: return launch_one<3, ALIGNED>(p, batch, s, e0, e1);
+        case 4: return launch_one<4, ALIGNED>(p, batch, s, e0, e1);
+        case 6: return launch_one<6, ALIGNED>(p, batch, s, e0, e1);
+        case 8: return launch_one<8, ALIGNED>(p, batch, s, e0, e1);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+#define PDA_CAT2(a, b, c) a##_##b##_##c
+#define PDA_CAT(a, b, c) PDA_CAT2(a, b, c)
+hipError_t PDA_CAT(launch_decode_valu, PDA_DTYPE, PDA_HEAD)(int gpad, bool aligned,
+                                                            const DecodeParams& p, int batch,
+                                                            hipStream_t stream, hipEvent_t e0,
+                                                            hipEvent_t e1) {
+    return aligned ? launch_gp<true>(gpad, p, batch, stream, e0, e1)
+                   : launch_gp<false>(gpad, p, batch, stream, e0, e1);
+}
+
+}  // namespace pda

@@ -1,0 +1,317 @@
+// Host runtime of libpda.so: argument validation, the partition plan, the
+// workspace layout and the kernel launches behind the C ABI of pda.h.
+#include <atomic>
+#include <stdint.h>
+
+#include "pda_common.h"
+
+namespace pda {
+// one definition per (element type, head size) translation unit
+hipError_t launch_decode_valu_0_64(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+hipError_t launch_decode_valu_0_128(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+hipError_t launch_decode_valu_0_256(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+hipError_t launch_decode_valu_1_64(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+hipError_t launch_decode_valu_1_128(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+hipError_t launch_decode_valu_1_256(int, bool, const DecodeParams&, int, hipStream_t,
+                                       hipEvent_t, hipEvent_t);
+
+hipError_t launch_decode_valu(int dtype, int head_size, int gpad, bool aligned,
+                              const DecodeParams& p, int batch, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
+    if (dtype == PDA_BF16) {
+        if (head_size == 64) return launch_decode_valu_0_64(gpad, aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_valu_0_128(gpad, aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_valu_0_256(gpad, aligned, p, batch, s, e0, e1);
+    } else {
+        if (head_size == 64) return launch_decode_valu_1_64(gpad, aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_valu_1_128(gpad, aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_valu_1_256(gpad, aligned, p, batch, s, e0, e1);
+    }
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cu_count[kMaxDevices];
+constexpr int64_t kMaxLdsBytes = 64 * 1024;
+constexpr int32_t kMaxSeqLen = 1 << 30;
+constexpr int32_t kMaxGridYZ = 65535;
+// the VALU kernel is compiled for packed groups up to 8 heads
+constexpr int kValuMaxGroup = 8;
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round256(int64_t x) { return cdiv64(x, 256) * 256; }
+
+// tokens per wavefront tile of the VALU kernel: the block size must be a
+// multiple of it for the one-lookup-per-tile path
+int valu_tile(int head_size) { return head_size == 256 ? 8 : 16; }
+
+int64_t table_capacity(const pda_shape_t* s, const pda_plan_t* pl) {
+    return (int64_t)pl->tokens_per_partition / s->block_size + 2;
+}
+
+int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
+    if (!pl) return PDA_ERR_INVALID;
+    if (pl->num_partitions < 1 || pl->tokens_per_partition < PDA_TP_ALIGN ||
+        pl->tokens_per_partition % PDA_TP_ALIGN != 0)
+        return PDA_ERR_INVALID;
+    if ((int64_t)pl->num_partitions * pl->tokens_per_partition < (int64_t)s->max_seq_len)
+        return PDA_ERR_INVALID;
+    if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen)
+        return PDA_ERR_UNSUPPORTED;
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (pl->variant == PDA_VARIANT_VALU) {
+        if (G > kValuMaxGroup) return PDA_ERR_UNSUPPORTED;
+        const int64_t lds = (int64_t)decode_lds_bytes(s->head_size, valu_group_pad(G),
+                                                      (int)table_capacity(s, pl));
+        if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
+    } else if (pl->variant == PDA_VARIANT_MFMA) {
+        return PDA_ERR_UNSUPPORTED;  // not built in this library version
+    } else {
+        return PDA_ERR_INVALID;
+    }
+    return PDA_OK;
+}
+
+int device_cu_count(int32_t* cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PDA_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return PDA_ERR_DEVICE;
+    int32_t c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            return PDA_ERR_DEVICE;
+        c = v;
+        g_cu_count[dev].store(c, std::memory_order_relaxed);
+    }
+    *cu = c;
+    return PDA_OK;
+}
+
+DecodeParams make_params(const pda_shape_t* s, const pda_plan_t* pl, float scale) {
+    DecodeParams p{};
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_q_heads = s->num_q_heads;
+    p.num_kv_heads = s->num_kv_heads;
+    p.group = s->num_q_heads / s->num_kv_heads;
+    p.block_size = s->block_size;
+    p.max_blocks_per_seq = s->max_blocks_per_seq;
+    p.max_seq_len = s->max_seq_len;
+    p.num_blocks = s->num_blocks;
+    p.num_partitions = pl->num_partitions;
+    p.tokens_per_part = pl->tokens_per_partition;
+    p.tbl_capacity = (int32_t)table_capacity(s, pl);
+    p.bs_div = make_fastdiv((uint32_t)s->block_size);
+    p.head_stride = s->block_size * s->head_size;
+    p.block_stride = (int64_t)s->num_kv_heads * p.head_stride;
+    return p;
+}
+
+}  // namespace
+}  // namespace pda
+
+using namespace pda;
+
+extern "C" {
+
+int pda_check_shape(const pda_shape_t* s) {
+    if (!s) return PDA_ERR_INVALID;
+    if (s->num_seqs < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->block_size < 1 ||
+        s->num_blocks < 1 || s->max_blocks_per_seq < 1 || s->max_seq_len < 0)
+        return PDA_ERR_INVALID;
+    if (s->num_q_heads % s->num_kv_heads != 0) return PDA_ERR_INVALID;
+    if (s->head_size != 64 && s->head_size != 128 && s->head_size != 256)
+        return PDA_ERR_UNSUPPORTED;
+    if (s->dtype != PDA_BF16 && s->dtype != PDA_FP16) return PDA_ERR_UNSUPPORTED;
+    if (s->num_q_heads / s->num_kv_heads > PDA_MAX_GROUP) return PDA_ERR_UNSUPPORTED;
+    if ((int64_t)s->max_seq_len > (int64_t)s->max_blocks_per_seq * s->block_size)
+        return PDA_ERR_INVALID;
+    if (s->max_seq_len > kMaxSeqLen) return PDA_ERR_UNSUPPORTED;
+    if (s->num_seqs > kMaxGridYZ || s->num_kv_heads > kMaxGridYZ ||
+        s->num_q_heads > kMaxGridYZ)
+        return PDA_ERR_UNSUPPORTED;
+    return PDA_OK;
+}
+
+int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    if (!plan || cu_count < 1) return PDA_ERR_INVALID;
+    // the rule documented in pda.h
+    const int64_t bpt = 4 * (int64_t)s->head_size;
+    const int64_t align = PDA_TP_ALIGN;
+    int64_t t_min = (PDA_WG_MIN_BYTES / bpt / align) * align;
+    if (t_min < align) t_min = align;
+    int64_t t_max = (PDA_WG_MAX_BYTES / bpt / align) * align;
+    if (t_max < t_min) t_max = t_min;
+    const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
+    const int64_t p_tgt = cdiv64((int64_t)PDA_WG_PER_CU * cu_count, units);
+    int64_t tp;
+    if (s->max_seq_len <= 0) {
+        tp = t_min;
+    } else {
+        tp = cdiv64(cdiv64(s->max_seq_len, p_tgt), align) * align;
+        if (tp < t_min) tp = t_min;
+        if (tp > t_max) tp = t_max;
+    }
+    int64_t P = cdiv64(s->max_seq_len, tp);
+    if (P < 1) P = 1;
+    plan->num_partitions = (int32_t)P;
+    plan->tokens_per_partition = (int32_t)tp;
+    plan->variant = PDA_VARIANT_VALU;
+    plan->cu_count = cu_count;
+    plan->workspace_bytes = pda_workspace_bytes(s, plan);
+    return PDA_OK;
+}
+
+int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
+    if (!s || !pl) return PDA_ERR_INVALID;
+    if (pl->num_partitions <= 1) return 0;
+    const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
+    return round256(rows * s->head_size * 4) + round256(rows * 2 * 4);
+}
+
+int paged_decode_attn_plan(const pda_shape_t* s, pda_plan_t* plan) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    if (!plan) return PDA_ERR_INVALID;
+    int32_t cu = 0;
+    rc = device_cu_count(&cu);
+    if (rc != PDA_OK) return rc;
+    return pda_plan_for_cus(s, cu, plan);
+}
+
+int64_t paged_decode_attn_workspace_size(const pda_shape_t* s) {
+    pda_plan_t pl;
+    int rc = paged_decode_attn_plan(s, &pl);
+    if (rc != PDA_OK) return rc;
+    return pl.workspace_bytes;
+}
+
+static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float scale, void* out, void* workspace,
+                      int64_t workspace_bytes, void* stream, hipEvent_t ev0, hipEvent_t ev1) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    rc = check_plan(s, pl);
+    if (rc != PDA_OK) return rc;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PDA_ERR_INVALID;
+    const int64_t need = pda_workspace_bytes(s, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PDA_ERR_WORKSPACE;
+
+    DecodeParams p = make_params(s, pl, scale);
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.out = out;
+    if (need > 0) {
+        const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
+        p.ws_o = static_cast<float*>(workspace);
+        p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           round256(rows * s->head_size * 4));
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = p.group;
+    const bool aligned = s->block_size % valu_tile(s->head_size) == 0;
+    hipError_t e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(G), aligned, p,
+                                      s->num_seqs, st, ev0, ev1);
+    if (e != hipSuccess) return PDA_ERR_LAUNCH;
+    if (pl->num_partitions > 1) {
+        e = launch_merge(s->dtype, s->head_size, p, s->num_seqs, st);
+        if (e != hipSuccess) return PDA_ERR_LAUNCH;
+    }
+    return PDA_OK;
+}
+
+int paged_decode_attn_with_plan(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                float scale, void* out, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+    return run_decode(s, pl, q, k_cache, v_cache, block_table, seq_lens, scale, out, workspace,
+                      workspace_bytes, stream, nullptr, nullptr);
+}
+
+int paged_decode_attn_timed(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* seq_lens, float scale,
+                            void* out, void* workspace, int64_t workspace_bytes,
+                            void* start_event, void* stop_event, void* stream) {
+    pda_plan_t own;
+    if (!pl) {
+        int rc = paged_decode_attn_plan(s, &own);
+        if (rc != PDA_OK) return rc;
+        pl = &own;
+    }
+    return run_decode(s, pl, q, k_cache, v_cache, block_table, seq_lens, scale, out, workspace,
+                      workspace_bytes, stream, static_cast<hipEvent_t>(start_event),
+                      static_cast<hipEvent_t>(stop_event));
+}
+
+int paged_decode_attn(const pda_shape_t* s, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, void* out, void* workspace, int64_t workspace_bytes,
+                      void* stream) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PDA_ERR_INVALID;
+    pda_plan_t pl;
+    rc = paged_decode_attn_plan(s, &pl);
+    if (rc != PDA_OK) return rc;
+    return paged_decode_attn_with_plan(s, &pl, q, k_cache, v_cache, block_table, seq_lens, scale,
+                                       out, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t* trace_slot, int32_t* trace_part, int32_t* trace_range,
+                            void* stream) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    rc = check_plan(s, pl);
+    if (rc != PDA_OK) return rc;
+    if (!block_table || !seq_lens || !trace_slot || !trace_part || !trace_range)
+        return PDA_ERR_INVALID;
+    DecodeParams p = make_params(s, pl, 1.0f);
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.trace_slot = trace_slot;
+    p.trace_part = trace_part;
+    p.trace_range = trace_range;
+    const bool aligned = s->block_size % valu_tile(s->head_size) == 0;
+    hipError_t e = launch_trace(s->head_size, aligned, p, s->num_seqs,
+                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
+}
+
+const char* pda_status_string(int status) {
+    switch (status) {
+        case PDA_OK: return "ok";
+        case PDA_ERR_INVALID: return "invalid argument";
+        case PDA_ERR_UNSUPPORTED: return "unsupported shape or type";
+        case PDA_ERR_WORKSPACE: return "workspace too small";
+        case PDA_ERR_LAUNCH: return "kernel launch failed";
+        case PDA_ERR_DEVICE: return "device query failed";
+        default: return "unknown status";
+    }
+}
+
+#ifndef PDA_BUILD_FLAGS
+#define PDA_BUILD_FLAGS "unknown"
+#endif
+const char* pda_build_id(void) {
+    return "libpda 0.1.0; target gfx950; variants valu; flags " PDA_BUILD_FLAGS;
+}
+
+}  // extern "C"

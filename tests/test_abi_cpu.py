@@ -1,0 +1,162 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, its plan equals the independently re-derived plan bit for
+bit, and invalid arguments are rejected by host validation before anything
+is launched (no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_decode_amd as pda
+from oracle import plan as oplan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pda.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pda.load_library()
+    names = header_functions()
+    assert "paged_decode_attn" in names and "paged_decode_attn_workspace_size" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in pda.pda_build_id()
+
+
+def test_status_strings():
+    for s in (pda.PDA_OK, pda.PDA_ERR_INVALID, pda.PDA_ERR_UNSUPPORTED, pda.PDA_ERR_WORKSPACE,
+              pda.PDA_ERR_LAUNCH, pda.PDA_ERR_DEVICE):
+        assert pda.pda_status_string(s) != "unknown status"
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_plan_matches_oracle_plan(D):
+    rng = np.random.default_rng(1000 + D)
+    for _ in range(3000):
+        B = int(rng.integers(1, 200))
+        Hkv = int(rng.integers(1, 17))
+        G = int(rng.integers(1, 9))
+        bs = int(rng.choice([1, 3, 16, 784]))
+        L = int(rng.integers(0, 300000))
+        mbs = max(1, -(-L // bs))
+        cu = int(rng.choice([1, 7, 80, 256, 304]))
+        shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16")
+        got = pda.pda_plan_for_cus(shape, cu)
+        P, T = oplan.partition(B, Hkv, D, L, cu)
+        assert (got.num_partitions, got.tokens_per_partition) == (P, T)
+        assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P)
+        assert got.cu_count == cu
+
+
+def test_plan_golden_through_library():
+    import json
+    with open(os.path.join(ROOT, "tests", "golden", "plan_cu256.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        shape = pda.make_shape(c["B"], c["Hkv"] * 2, c["Hkv"], c["D"], 16, 1,
+                               max(1, -(-c["Lmax"] // 16)), c["Lmax"])
+        got = pda.pda_plan_for_cus(shape, g["cu_count"])
+        assert (got.num_partitions, got.tokens_per_partition) == (c["P"], c["T_p"]), c["name"]
+
+
+BAD_SHAPES = [
+    (dict(num_seqs=0), pda.PDA_ERR_INVALID),
+    (dict(num_q_heads=12, num_kv_heads=8), pda.PDA_ERR_INVALID),
+    (dict(head_size=96), pda.PDA_ERR_UNSUPPORTED),
+    (dict(head_size=512), pda.PDA_ERR_UNSUPPORTED),
+    (dict(dtype=2), pda.PDA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=17 * 8), pda.PDA_ERR_UNSUPPORTED),
+    (dict(block_size=0), pda.PDA_ERR_INVALID),
+    (dict(max_seq_len=-1), pda.PDA_ERR_INVALID),
+    (dict(max_seq_len=16 * 4 + 1), pda.PDA_ERR_INVALID),  # > MBS * bs
+    (dict(num_blocks=0), pda.PDA_ERR_INVALID),
+]
+
+
+def _shape(**kw):
+    base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_size=128, block_size=16,
+                num_blocks=16, max_blocks_per_seq=4, max_seq_len=64, dtype=0)
+    base.update(kw)
+    return pda.PdaShape(**base)
+
+
+@pytest.mark.parametrize("kw,status", BAD_SHAPES)
+def test_invalid_shapes_rejected(kw, status):
+    assert pda.pda_check_shape(_shape(**kw)) == status
+    lib = pda.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    rc = lib.paged_decode_attn(ctypes.byref(_shape(**kw)), fake, fake, fake, fake, fake, 1.0,
+                               fake, None, 0, None)
+    assert rc == status
+
+
+def test_null_pointers_rejected_before_launch():
+    lib = pda.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    s = _shape()
+    args = [fake] * 5
+    for i in range(6):
+        ptrs = [fake] * 6
+        ptrs[i] = None
+        rc = lib.paged_decode_attn(ctypes.byref(s), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4],
+                                   1.0, ptrs[5], None, 0, None)
+        assert rc == pda.PDA_ERR_INVALID
+    del args
+
+
+def test_small_workspace_rejected_before_launch():
+    lib = pda.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    s = _shape(max_seq_len=64, max_blocks_per_seq=4)
+    plan = pda.PdaPlan(num_partitions=2, tokens_per_partition=64, variant=pda.PDA_VARIANT_VALU,
+                       cu_count=1, workspace_bytes=0)
+    need = pda.pda_workspace_bytes(s, plan)
+    assert need > 0
+    for ws, nbytes in ((None, 0), (fake, need - 1)):
+        rc = lib.paged_decode_attn_with_plan(ctypes.byref(s), ctypes.byref(plan), fake, fake, fake,
+                                             fake, fake, 1.0, fake, ws, nbytes, None)
+        assert rc == pda.PDA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("P,T,variant,status", [
+    (0, 64, 1, pda.PDA_ERR_INVALID),          # no partition
+    (1, 32, 1, pda.PDA_ERR_INVALID),          # not a multiple of 64
+    (1, 64, 1, pda.PDA_ERR_INVALID),          # does not cover max_seq_len = 100
+    (2, 64, 7, pda.PDA_ERR_INVALID),          # unknown variant
+])
+def test_bad_plans_rejected(P, T, variant, status):
+    lib = pda.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    s = _shape(max_seq_len=100, max_blocks_per_seq=7)
+    plan = pda.PdaPlan(num_partitions=P, tokens_per_partition=T, variant=variant, cu_count=1,
+                       workspace_bytes=0)
+    rc = lib.paged_decode_attn_with_plan(ctypes.byref(s), ctypes.byref(plan), fake, fake, fake,
+                                         fake, fake, 1.0, fake, fake, 1 << 30, None)
+    assert rc == status
+
+
+def test_fastdiv_method_is_exact():
+    """The multiply-high division the kernels use for token -> (block, slot),
+    checked as arithmetic over block sizes 1..2048 and 784 on dividends
+    including the extremes below 2^31.  (The GPU trace test checks the
+    compiled kernels against the oracle's plain division.)"""
+    rng = np.random.default_rng(7)
+    ns = np.concatenate([np.arange(0, 5000), rng.integers(0, 2 ** 31, 20000),
+                         np.array([2 ** 31 - 1, 2 ** 31 - 2])]).astype(np.uint64)
+    for d in list(range(1, 2049)) + [784, 65535, 1 << 20, 12345677]:
+        l = 0
+        while (1 << l) < d:
+            l += 1
+        mul = ((((1 << l) - d) << 32) // d + 1) & 0xFFFFFFFF
+        hi = (ns * np.uint64(mul)) >> np.uint64(32)
+        q = (hi + ns) >> np.uint64(l)
+        assert np.array_equal(q, ns // np.uint64(d)), d
