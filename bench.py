@@ -58,7 +58,9 @@ def time_case(case, steps, warmup, passes=1):
                            case.max_blocks_per_seq, case.max_seq_len, case.dtype)
     plan = pda.paged_decode_attn_plan(shape)
     out = torch.empty_like(case.q)
-    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=case.q.device)
+    ws = torch.empty(max(1, pda.pda_workspace_bytes(shape, plan)), dtype=torch.uint8,
+                     device=case.q.device)
+    pda.paged_decode_attn_workspace_init(ws)
     reps = replicas_for(case)
     R = len(reps)
 

@@ -96,16 +96,30 @@ extern "C" {
  * Partition p of (b, g) covers tokens [p*T_p, min((p+1)*T_p, seq_lens[b]));
  * it is empty when p*T_p >= seq_lens[b].  The grid of the main kernel is
  * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
- * workspace is used; otherwise it writes fp32 partials and a merge kernel
- * combines them, and the workspace holds
- *   partial outputs  [B][Hq][P][D] fp32, then (m, l) pairs [B][Hq][P][2] fp32,
- * each part aligned to 256 bytes. */
+ * workspace is used; otherwise it writes fp32 partials that are merged with
+ * the log-sum-exp rule, either
+ *   PDA_MERGE_KERNEL by a separate merge kernel on the same stream (the
+ *                    plan's choice: the merge is spread over D/64 x Hq x B
+ *                    workgroups), or
+ *   PDA_MERGE_FUSED  by the last workgroup of each (b, g) to finish, found
+ *                    with an atomic counter in the workspace (one launch;
+ *                    that workgroup alone reads P x G x D partials, which
+ *                    only pays when that product is small).
+ * The workspace holds partial outputs [B][Hq][P][D] fp32, then (m, l) pairs
+ * [B][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
+ * aligned to 256 bytes.  The counters must be zero when a fused call starts;
+ * every fused call leaves them zero again, so a workspace needs zeroing once
+ * (paged_decode_attn_workspace_init, or any zero fill) before its first use.
+ * Calls that run concurrently need separate workspaces. */
 #define PDA_TILE          16
 #define PDA_WAVES         4
 #define PDA_TP_ALIGN      64
 #define PDA_WG_PER_CU     2
 #define PDA_WG_MIN_BYTES  (64 * 1024)
 #define PDA_WG_MAX_BYTES  (512 * 1024)
+
+#define PDA_MERGE_FUSED   0
+#define PDA_MERGE_KERNEL  1
 
 typedef struct pda_shape {
     int32_t num_seqs;            /* B >= 1 */
@@ -123,6 +137,7 @@ typedef struct pda_plan {
     int32_t num_partitions;        /* P >= 1 */
     int32_t tokens_per_partition;  /* T_p, a positive multiple of PDA_TP_ALIGN */
     int32_t variant;               /* PDA_VARIANT_VALU or PDA_VARIANT_MFMA */
+    int32_t merge;                 /* PDA_MERGE_KERNEL (the plan's choice) or PDA_MERGE_FUSED */
     int32_t cu_count;              /* the C the plan was made for */
     int64_t workspace_bytes;       /* 0 when P == 1 */
 } pda_plan_t;
@@ -145,7 +160,12 @@ int64_t paged_decode_attn_workspace_size(const pda_shape_t* shape);
 /* Workspace bytes a given plan needs (0 when plan->num_partitions == 1). */
 int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
 
-/* The decode step.
+/* Zero `bytes` of a device workspace on `stream` (asynchronously): the state
+ * a workspace must be in before its first fused call.  Call it once after
+ * allocating a workspace, outside any HIP graph capture. */
+int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream);
+
+/* The decode step, under the device's own plan.
  *   q            [B][Hq][D]           16-bit, the one query token per sequence
  *   k_cache      [NB][Hkv][bs][D]     16-bit, the paged K pool
  *   v_cache      [NB][Hkv][bs][D]     16-bit, the paged V pool (same layout)
@@ -154,7 +174,7 @@ int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(D))
  *   out          [B][Hq][D]           16-bit, written in full
  *   workspace    device scratch of workspace_bytes (may be NULL if the plan
- *                needs none); its contents on entry do not matter
+ *                needs none), zeroed once before its first use (see above)
  * Returns PDA_OK once the kernels are enqueued on `stream`. */
 int paged_decode_attn(const pda_shape_t* shape,
                       const void* q, const void* k_cache, const void* v_cache,

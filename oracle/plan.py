@@ -47,12 +47,16 @@ def partition(num_seqs: int, num_kv_heads: int, head_size: int, max_seq_len: int
     return p, t_p
 
 
-def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int) -> int:
-    """Partial outputs [B][Hq][P][D] fp32 then (m, l) [B][Hq][P][2] fp32, each
-    part rounded up to 256 bytes; none when P == 1."""
+def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,
+                    num_kv_heads: int = 1) -> int:
+    """Partial outputs [B][Hq][P][D] fp32, then (m, l) [B][Hq][P][2] fp32,
+    then arrival counters [B][Hkv] int32, each part rounded up to 256 bytes;
+    none when P == 1."""
     if p <= 1:
         return 0
 
     def r256(x):
         return _cdiv(x, 256) * 256
-    return r256(num_seqs * num_q_heads * p * head_size * 4) + r256(num_seqs * num_q_heads * p * 2 * 4)
+    return (r256(num_seqs * num_q_heads * p * head_size * 4)
+            + r256(num_seqs * num_q_heads * p * 2 * 4)
+            + r256(num_seqs * num_kv_heads * 4))

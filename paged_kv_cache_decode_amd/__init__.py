@@ -29,6 +29,8 @@ PDA_BF16 = 0
 PDA_FP16 = 1
 PDA_VARIANT_VALU = 1
 PDA_VARIANT_MFMA = 2
+PDA_MERGE_FUSED = 0
+PDA_MERGE_KERNEL = 1
 
 _DTYPES = {"bf16": PDA_BF16, "fp16": PDA_FP16}
 
@@ -43,7 +45,8 @@ class PdaShape(ctypes.Structure):
 
 class PdaPlan(ctypes.Structure):
     _fields_ = [("num_partitions", ctypes.c_int32), ("tokens_per_partition", ctypes.c_int32),
-                ("variant", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("cu_count", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
@@ -89,6 +92,8 @@ def load_library():
     lib.paged_decode_attn_timed.restype = ctypes.c_int
     lib.paged_decode_attn_trace.argtypes = [sp, pp, P, P, P, P, P, P]
     lib.paged_decode_attn_trace.restype = ctypes.c_int
+    lib.paged_decode_attn_workspace_init.argtypes = [P, ctypes.c_int64, P]
+    lib.paged_decode_attn_workspace_init.restype = ctypes.c_int
     lib.pda_status_string.argtypes = [ctypes.c_int]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_build_id.argtypes = []
@@ -210,7 +215,7 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
     else:
         need = pda_workspace_bytes(shape, plan)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zeroed, as required
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if plan is None:
         rc = lib.paged_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -232,6 +237,14 @@ def paged_decode_attn_with_plan(q, k_cache, v_cache, block_table, seq_lens, scal
     return paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale, out=out,
                              workspace=workspace, max_seq_len=max_seq_len, plan=plan,
                              stream=stream)
+
+
+def paged_decode_attn_workspace_init(workspace, stream=None):
+    """Zero a workspace tensor on the stream (needed once before its first use)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load_library().paged_decode_attn_workspace_init(_ptr(workspace), nbytes, _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_workspace_init")
 
 
 def paged_decode_attn_timed(shape: PdaShape, plan: Optional[PdaPlan], q, k_cache, v_cache,

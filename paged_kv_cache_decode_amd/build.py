@@ -24,23 +24,23 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _units():
+def _units(csrc=CSRC):
     units = []
     for dt in (0, 1):
         for hd in (64, 128, 256):
-            units.append((os.path.join(CSRC, "pda_decode_valu.hip"),
+            units.append((os.path.join(csrc, "pda_decode_valu.hip"),
                           f"valu_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
-    units.append((os.path.join(CSRC, "pda_merge.hip"), "merge.o", []))
-    units.append((os.path.join(CSRC, "pda_trace.hip"), "trace.o", []))
+    units.append((os.path.join(csrc, "pda_merge.hip"), "merge.o", []))
+    units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
     flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops"])
-    units.append((os.path.join(CSRC, "pda_host.cpp"), "host.o",
+    units.append((os.path.join(csrc, "pda_host.cpp"), "host.o",
                    ["-x", "hip", f'-DPDA_BUILD_FLAGS="{flags}"']))
     return units
 
 
-def _compile(unit, verbose):
+def _compile(unit, verbose, build_dir):
     src, obj, extra = unit
-    out = os.path.join(BUILD, obj)
+    out = os.path.join(build_dir, obj)
     cmd = [HIPCC] + CFLAGS + extra + ["-c", src, "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -54,17 +54,21 @@ def _compile(unit, verbose):
     return out
 
 
-def build_library(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    units = _units()
+def build_library(verbose: bool = False, jobs: int = 8, out: str = LIB,
+                  defines=(), build_dir: str = BUILD, csrc: str = CSRC) -> str:
+    """Compile and link; `defines` are extra -D flags (tuning variants),
+    `csrc` another copy of the sources."""
+    os.makedirs(build_dir, exist_ok=True)
+    units = [(src, obj, extra + [f"-D{d}" for d in defines])
+             for src, obj, extra in _units(csrc)]
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, 16))) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), units))
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+        objs = list(ex.map(lambda u: _compile(u, verbose, build_dir), units))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

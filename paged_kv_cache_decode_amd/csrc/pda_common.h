@@ -53,6 +53,7 @@ struct DecodeParams {
     void* out;                 // [B][Hq][D]
     float* ws_o;               // [B][Hq][P][D]    (P > 1 only)
     float* ws_ml;              // [B][Hq][P][2]    (P > 1 only)
+    int32_t* counters;         // [B][Hkv] arrival counters (fused merge)
     int32_t* trace_slot;       // trace kernel only
     int32_t* trace_part;
     int32_t* trace_range;
@@ -67,6 +68,7 @@ struct DecodeParams {
     int32_t num_partitions;    // P
     int32_t tokens_per_part;   // T_p
     int32_t tbl_capacity;      // LDS entries reserved for the block-table slice
+    int32_t fused_merge;       // 1: the last unit of each (b, g) merges the partials
     FastDiv bs_div;
     int64_t block_stride;      // Hkv * bs * D elements
     int32_t head_stride;       // bs * D elements
@@ -75,6 +77,7 @@ struct DecodeParams {
 constexpr int kWave = 64;
 constexpr int kWaves = PDA_WAVES;
 constexpr int kTile = PDA_TILE;
+constexpr int kAlignTokens = 16;
 constexpr int kThreads = kWave * kWaves;
 
 // Launchers (one translation unit per element type and head size).

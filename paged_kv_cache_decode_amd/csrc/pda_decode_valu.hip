@@ -33,7 +33,45 @@
 #error "PDA_HEAD must be defined"
 #endif
 
+#ifndef PDA_VALU_STAGES
+#define PDA_VALU_STAGES 2
+#endif
+#if PDA_VALU_SCHED_FENCE
+#define PDA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define PDA_SCHED_FENCE() ((void)0)
+#endif
+
 namespace pda {
+
+// Log-sum-exp merge of the Pb partials (o_p normalised, m_p, l_p in the exp2
+// domain) of the G heads of unit (b, g), one output element per thread and
+// step, partitions in index order with a running max:
+//   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p.
+template <typename Elt, int D>
+__device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+    const int G = p.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int i = idx / D, d = idx - i * D;
+        const int64_t row = (int64_t)b * p.num_q_heads + g * G + i;
+        const float* ml = p.ws_ml + row * p.num_partitions * 2;
+        const float* po = p.ws_o + row * p.num_partitions * D + d;
+        float M = -FLT_MAX, o = 0.f, den = 0.f;
+#pragma unroll 8
+        for (int q = 0; q < Pb; ++q) {
+            const float2 mlq = make_float2(load_coherent(ml + 2 * q), load_coherent(ml + 2 * q + 1));
+            const float oq = load_coherent(po + (int64_t)q * D);
+            const float mn = fmaxf(M, mlq.x);
+            const float sc = fast_exp2(M - mn);
+            const float w = mlq.y * fast_exp2(mlq.x - mn);
+            o = o * sc + w * oq;
+            den = den * sc + w;
+            M = mn;
+        }
+        out16[row * D + d] = Elt::from_float(o / den);
+    }
+}
 
 // The element type and head size are template parameters of the kernel (not
 // only of this translation unit) so that every instantiation has its own
@@ -47,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
 
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int c = lane % LPT, r = lane / LPT;
     const int G = p.group;
     const int L = context_len(p, b);
@@ -55,8 +94,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const bool direct = p.num_partitions == 1;
     uint16_t* out16 = static_cast<uint16_t*>(p.out);
 
-    if (t0 >= L) {  // empty partition; with one partition this is L == 0
-        if (direct)
+    if (t0 >= L) {  // empty partition; the first one of an empty context writes zeros
+        if (part == 0)
             for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
                 out16[((int64_t)b * p.num_q_heads + g * G) * D + idx] = 0;
         return;
@@ -78,20 +117,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    const uint16_t* kc = static_cast<const uint16_t*>(p.k_cache);
-    const uint16_t* vc = static_cast<const uint16_t*>(p.v_cache);
-    const int64_t head_off = (int64_t)g * p.head_stride + c * 8;
+    const char* kc = static_cast<const char*>(p.k_cache);
+    const char* vc = static_cast<const char*>(p.v_cache);
+    const int64_t head_off = (int64_t)g * p.head_stride;   // elements
+    const uint32_t lane_off = (uint32_t)c * 16;            // bytes
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
+    // Address of a round's row: a block base (wave-uniform on the aligned
+    // path, so it stays in scalar registers) plus a 32-bit per-lane byte
+    // offset, the form of a global load with a scalar base.
     auto load_tile = [&](int j, uint4 (&kr)[U], uint4 (&vr)[U]) {
         const int tile_base = t0 + j * TT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int phys, slot;
-            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot);
-            const int64_t off = (int64_t)phys * p.block_stride + head_off + (int64_t)slot * D;
-            kr[u] = *reinterpret_cast<const uint4*>(kc + off);
-            vr[u] = *reinterpret_cast<const uint4*>(vc + off);
+            int phys, slot0, dt;
+            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
+            const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+            const uint32_t off = (uint32_t)dt * (2 * D) + lane_off;
+            kr[u] = load_row16(kc + base + off);
+            vr[u] = load_row16(vc + base + off);
         }
     };
 
@@ -104,14 +148,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
     }
 
-    int j = wave;
-    uint4 kr[U], vr[U];
-    if (j < ntiles) load_tile(j, kr, vr);
-    for (; j < ntiles; j += kWaves) {
-        // prefetch the wave's next tile (the last iteration re-reads its own)
-        uint4 kn[U], vn[U];
-        load_tile(min(j + kWaves, ntiles - 1), kn, vn);
-
+    // One tile of QK^T, masking, online softmax and PV for this lane.
+    auto process = [&](int j, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
         const int tile_base = t0 + j * TT;
         const bool full = tile_base + TT <= t1;
         float s[U][GP];
@@ -147,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
             for (int i = 0; i < GP; ++i) {
-                const float alpha = exp2f(m[i] - mn[i]);
+                const float alpha = fast_exp2(m[i] - mn[i]);
                 l[i] *= alpha;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[i][e] *= alpha;
@@ -163,15 +201,58 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
             vf[6] = Elt::lo(vr[u].w); vf[7] = Elt::hi(vr[u].w);
 #pragma unroll
             for (int i = 0; i < GP; ++i) {
-                const float pw = exp2f(s[u][i] - m[i]);
+                const float pw = fast_exp2(s[u][i] - m[i]);
                 l[i] += pw;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(pw, vf[e], acc[i][e]);
             }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) { kr[u] = kn[u]; vr[u] = vn[u]; }
+    };
+
+    // Register buffers in rotation: while one tile is processed the wave's
+    // next tile(s) are already in flight, and no buffer is ever copied (a copy
+    // would force a wait for the in-flight loads).  A load past the
+    // partition's last tile re-reads that tile (a cache hit) to keep the loop
+    // body free of branches around loads.
+    const auto clampt = [&](int jj) { return min(jj, ntiles - 1); };
+    int j = wave;
+#if PDA_VALU_STAGES == 3
+    uint4 ka[U], va[U], kb[U], vb[U], kx[U], vx[U];
+    if (j < ntiles) {
+        load_tile(j, ka, va);
+        load_tile(clampt(j + kWaves), kb, vb);
     }
+    for (; j < ntiles; j += 3 * kWaves) {
+        load_tile(clampt(j + 2 * kWaves), kx, vx);
+        PDA_SCHED_FENCE();
+        process(j, ka, va);
+        if (j + kWaves >= ntiles) break;
+        load_tile(clampt(j + 3 * kWaves), ka, va);
+        PDA_SCHED_FENCE();
+        process(j + kWaves, kb, vb);
+        if (j + 2 * kWaves >= ntiles) break;
+        load_tile(clampt(j + 4 * kWaves), kb, vb);
+        PDA_SCHED_FENCE();
+        process(j + 2 * kWaves, kx, vx);
+    }
+#else
+    // Loop rotated so that its head is a wait for buffer a while buffer b is
+    // already in flight.
+    uint4 ka[U], va[U], kb[U], vb[U];
+    if (j < ntiles) {
+        load_tile(j, ka, va);
+        load_tile(clampt(j + kWaves), kb, vb);
+    }
+    for (; j < ntiles; j += 2 * kWaves) {
+        process(j, ka, va);
+        if (j + kWaves >= ntiles) break;
+        load_tile(clampt(j + 2 * kWaves), ka, va);
+        PDA_SCHED_FENCE();
+        process(j + kWaves, kb, vb);
+        load_tile(clampt(j + 3 * kWaves), kb, vb);
+        PDA_SCHED_FENCE();
+    }
+#endif
 
     // merge the R lane sub-streams (lanes c, c+LPT, ...) of the wavefront
 #pragma unroll
@@ -181,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
             const float mo = __shfl_xor(m[i], x);
             const float lo = __shfl_xor(l[i], x);
             const float mm = fmaxf(m[i], mo);
-            const float wa = exp2f(m[i] - mm), wb = exp2f(mo - mm);
+            const float wa = fast_exp2(m[i] - mm), wb = fast_exp2(mo - mm);
             l[i] = l[i] * wa + lo * wb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -212,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float* row = red + (w * GP + i) * (D + 2);
-            const float wt = exp2f(row[D] - M);
+            const float wt = fast_exp2(row[D] - M);
             den += row[D + 1] * wt;
             o += row[d] * wt;
         }
@@ -221,10 +302,41 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
             out16[((int64_t)b * p.num_q_heads + h) * D + d] = Elt::from_float(o / den);
         } else {
             const int64_t prow = ((int64_t)b * p.num_q_heads + h) * p.num_partitions + part;
-            p.ws_o[prow * D + d] = o / den;
-            if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
+            if (p.fused_merge) {  // read back by another workgroup of this launch
+                store_coherent(p.ws_o + prow * D + d, o / den);
+                if (d == 0) {
+                    store_coherent(p.ws_ml + prow * 2, M);
+                    store_coherent(p.ws_ml + prow * 2 + 1, den);
+                }
+            } else {              // read by the merge kernel after this launch
+                p.ws_o[prow * D + d] = o / den;
+                if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
+            }
         }
     }
+    if (direct || !p.fused_merge) return;
+
+    // Fused split-KV merge: the unit that finishes last among the Pb non-empty
+    // partitions of (b, g) merges them.  The partials above were stored at
+    // device scope (write-through to the point where all XCDs see them); each
+    // wave waits for its stores to be acknowledged before the workgroup
+    // barrier, then thread 0 counts the arrival with a device-scope atomic.
+    // The last arrival resets the counter for the next call and reads the
+    // partials back with device-scope loads.  No L2 write-back or invalidate
+    // is needed.
+    __shared__ int s_last;
+    wait_stores_done();
+    __syncthreads();
+    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
+    if (threadIdx.x == 0) {
+        int32_t* ctr = p.counters + (int64_t)b * p.num_kv_heads + g;
+        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == Pb - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_unit<Elt, D>(p, b, g, Pb);
 }
 
 #if PDA_DTYPE == 0

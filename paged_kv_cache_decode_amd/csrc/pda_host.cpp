@@ -48,9 +48,9 @@ constexpr int kValuMaxGroup = 8;
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round256(int64_t x) { return cdiv64(x, 256) * 256; }
 
-// tokens per wavefront tile of the VALU kernel: the block size must be a
-// multiple of it for the one-lookup-per-tile path
-int valu_tile(int head_size) { return head_size == 256 ? 8 : 16; }
+// block sizes that are multiples of 16 tokens take the one-lookup-per-round
+// path of the kernels (kAlignTokens)
+bool block_aligned(const pda_shape_t* s) { return s->block_size % kAlignTokens == 0; }
 
 int64_t table_capacity(const pda_shape_t* s, const pda_plan_t* pl) {
     return (int64_t)pl->tokens_per_partition / s->block_size + 2;
@@ -65,6 +65,7 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
         return PDA_ERR_INVALID;
     if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen)
         return PDA_ERR_UNSUPPORTED;
+    if (pl->merge != PDA_MERGE_FUSED && pl->merge != PDA_MERGE_KERNEL) return PDA_ERR_INVALID;
     const int G = s->num_q_heads / s->num_kv_heads;
     if (pl->variant == PDA_VARIANT_VALU) {
         if (G > kValuMaxGroup) return PDA_ERR_UNSUPPORTED;
@@ -167,6 +168,7 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     plan->num_partitions = (int32_t)P;
     plan->tokens_per_partition = (int32_t)tp;
     plan->variant = PDA_VARIANT_VALU;
+    plan->merge = PDA_MERGE_KERNEL;
     plan->cu_count = cu_count;
     plan->workspace_bytes = pda_workspace_bytes(s, plan);
     return PDA_OK;
@@ -176,7 +178,15 @@ int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
     if (!s || !pl) return PDA_ERR_INVALID;
     if (pl->num_partitions <= 1) return 0;
     const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
-    return round256(rows * s->head_size * 4) + round256(rows * 2 * 4);
+    return round256(rows * s->head_size * 4) + round256(rows * 2 * 4) +
+           round256((int64_t)s->num_seqs * s->num_kv_heads * 4);
+}
+
+int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream) {
+    if (bytes < 0 || (bytes > 0 && !workspace)) return PDA_ERR_INVALID;
+    if (bytes == 0) return PDA_OK;
+    hipError_t e = hipMemsetAsync(workspace, 0, (size_t)bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
 }
 
 int paged_decode_attn_plan(const pda_shape_t* s, pda_plan_t* plan) {
@@ -217,17 +227,21 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
     p.out = out;
     if (need > 0) {
         const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
-        p.ws_o = static_cast<float*>(workspace);
-        p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                           round256(rows * s->head_size * 4));
+        char* ws = static_cast<char*>(workspace);
+        const int64_t o_bytes = round256(rows * s->head_size * 4);
+        const int64_t ml_bytes = round256(rows * 2 * 4);
+        p.ws_o = reinterpret_cast<float*>(ws);
+        p.ws_ml = reinterpret_cast<float*>(ws + o_bytes);
+        p.counters = reinterpret_cast<int32_t*>(ws + o_bytes + ml_bytes);
+        p.fused_merge = pl->merge == PDA_MERGE_FUSED;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = p.group;
-    const bool aligned = s->block_size % valu_tile(s->head_size) == 0;
+    const bool aligned = block_aligned(s);
     hipError_t e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(G), aligned, p,
                                       s->num_seqs, st, ev0, ev1);
     if (e != hipSuccess) return PDA_ERR_LAUNCH;
-    if (pl->num_partitions > 1) {
+    if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
         e = launch_merge(s->dtype, s->head_size, p, s->num_seqs, st);
         if (e != hipSuccess) return PDA_ERR_LAUNCH;
     }
@@ -289,7 +303,7 @@ int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl,
     p.trace_slot = trace_slot;
     p.trace_part = trace_part;
     p.trace_range = trace_range;
-    const bool aligned = s->block_size % valu_tile(s->head_size) == 0;
+    const bool aligned = block_aligned(s);
     hipError_t e = launch_trace(s->head_size, aligned, p, s->num_seqs,
                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
@@ -311,7 +325,7 @@ const char* pda_status_string(int status) {
 #define PDA_BUILD_FLAGS "unknown"
 #endif
 const char* pda_build_id(void) {
-    return "libpda 0.1.0; target gfx950; variants valu; flags " PDA_BUILD_FLAGS;
+    return "libpda 0.2.0; target gfx950; variants valu; merge fused|kernel; flags " PDA_BUILD_FLAGS;
 }
 
 }  // extern "C"

@@ -11,16 +11,18 @@
 //
 // One workgroup of 256 threads per (64-element chunk of D, query head,
 // sequence): 16 lanes x 4 elements cover the chunk, 16 partition groups
-// stride over p, and the groups are summed in a fixed order through LDS.
+// stride over p.  Each thread merges its partitions with a running max after
+// one batch of loads; the 16 groups are then combined in a fixed order
+// through LDS, so the result does not depend on timing.
 #include "pda_device.h"
 
 namespace pda {
 
 template <typename Elt, int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-    __shared__ float red_m[4];
+    constexpr int kBatch = 8;  // partitions per thread and memory round trip
     __shared__ float4 red_o[16][16];
-    __shared__ float red_w[16][16];
+    __shared__ float2 red_mw[16][16];
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, d4 = tid & 15, pg = tid >> 4;
     const int L = context_len(p, b);
@@ -32,38 +34,51 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
         if (pg == 0) { out[0] = 0; out[1] = 0; out[2] = 0; out[3] = 0; }
         return;
     }
-    const float* ml = p.ws_ml + row * p.num_partitions * 2;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.num_partitions;
     const float* po = p.ws_o + row * p.num_partitions * D + chunk * 64 + d4 * 4;
 
-    // M = max over non-empty partitions
-    float mloc = -INFINITY;
-    for (int q = tid; q < Pb; q += 256) mloc = fmaxf(mloc, ml[2 * q]);
+    // This thread's partitions pg, pg+16, ...: all loads of a batch are issued
+    // before any is used, then combined with a running max (exp2 domain).
+    float M = -FLT_MAX, W = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = pg; q0 < Pb; q0 += 16 * kBatch) {
+        float2 mlv[kBatch];
+        float4 ov[kBatch];
 #pragma unroll
-    for (int x = 1; x < 64; x <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, x));
-    if ((tid & 63) == 0) red_m[tid >> 6] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float wsum = 0.f;
-#pragma unroll 4
-    for (int q = pg; q < Pb; q += 16) {
-        const float w = ml[2 * q + 1] * exp2f(ml[2 * q] - M);
-        const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
-        o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
-        wsum += w;
+        for (int k = 0; k < kBatch; ++k) {
+            const int q = min(q0 + 16 * k, Pb - 1);
+            mlv[k] = ml[q];
+            ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (q0 + 16 * k >= Pb) break;
+            const float mn = fmaxf(M, mlv[k].x);
+            const float sc = fast_exp2(M - mn);
+            const float w = mlv[k].y * fast_exp2(mlv[k].x - mn);
+            O.x = O.x * sc + w * ov[k].x; O.y = O.y * sc + w * ov[k].y;
+            O.z = O.z * sc + w * ov[k].z; O.w = O.w * sc + w * ov[k].w;
+            W = W * sc + w;
+            M = mn;
+        }
     }
-    red_o[pg][d4] = o;
-    red_w[pg][d4] = wsum;
+    red_o[pg][d4] = O;
+    red_mw[pg][d4] = make_float2(M, W);
     __syncthreads();
     if (pg == 0) {
-        float4 s = red_o[0][d4];
-        float ws = red_w[0][d4];
+        // combine the 16 partition groups in a fixed order
+        float Mg = -FLT_MAX;
 #pragma unroll
-        for (int k = 1; k < 16; ++k) {
+        for (int k = 0; k < 16; ++k) Mg = fmaxf(Mg, red_mw[k][d4].x);
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        float ws = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float2 mw = red_mw[k][d4];
             const float4 t = red_o[k][d4];
-            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
-            ws += red_w[k][d4];
+            const float f = fast_exp2(mw.x - Mg);
+            s.x += f * t.x; s.y += f * t.y; s.z += f * t.z; s.w += f * t.w;
+            ws += f * mw.y;
         }
         out[0] = Elt::from_float(s.x / ws);
         out[1] = Elt::from_float(s.y / ws);

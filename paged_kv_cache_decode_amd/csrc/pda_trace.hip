@@ -15,7 +15,8 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U, TT = Geo::TT;
     extern __shared__ int32_t tbl[];
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane % LPT, r = lane / LPT;
     const int L = context_len(p, b);
     const int t0 = part * p.tokens_per_part;
@@ -35,12 +36,12 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
         const int tile_base = t0 + j * TT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int phys, slot;
-            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot);
+            int phys, slot0, dt;
+            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
             const int t = tile_base + u * R + r;
             if (c == 0 && t < t1) {
                 const int64_t at = unit * p.max_seq_len + t;
-                p.trace_slot[at] = phys * p.block_size + slot;
+                p.trace_slot[at] = phys * p.block_size + slot0 + dt;
                 p.trace_part[at] = part;
             }
         }

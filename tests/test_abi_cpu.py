@@ -53,7 +53,8 @@ def test_plan_matches_oracle_plan(D):
         got = pda.pda_plan_for_cus(shape, cu)
         P, T = oplan.partition(B, Hkv, D, L, cu)
         assert (got.num_partitions, got.tokens_per_partition) == (P, T)
-        assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P)
+        assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv)
+        assert got.merge == pda.PDA_MERGE_KERNEL
         assert got.cu_count == cu
 
 
@@ -118,7 +119,7 @@ def test_small_workspace_rejected_before_launch():
     fake = ctypes.c_void_p(0x1000)
     s = _shape(max_seq_len=64, max_blocks_per_seq=4)
     plan = pda.PdaPlan(num_partitions=2, tokens_per_partition=64, variant=pda.PDA_VARIANT_VALU,
-                       cu_count=1, workspace_bytes=0)
+                       merge=pda.PDA_MERGE_FUSED, cu_count=1, workspace_bytes=0)
     need = pda.pda_workspace_bytes(s, plan)
     assert need > 0
     for ws, nbytes in ((None, 0), (fake, need - 1)):
@@ -127,18 +128,19 @@ def test_small_workspace_rejected_before_launch():
         assert rc == pda.PDA_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("P,T,variant,status", [
-    (0, 64, 1, pda.PDA_ERR_INVALID),          # no partition
-    (1, 32, 1, pda.PDA_ERR_INVALID),          # not a multiple of 64
-    (1, 64, 1, pda.PDA_ERR_INVALID),          # does not cover max_seq_len = 100
-    (2, 64, 7, pda.PDA_ERR_INVALID),          # unknown variant
+@pytest.mark.parametrize("P,T,variant,merge,status", [
+    (0, 64, 1, 0, pda.PDA_ERR_INVALID),          # no partition
+    (1, 32, 1, 0, pda.PDA_ERR_INVALID),          # not a multiple of 64
+    (1, 64, 1, 0, pda.PDA_ERR_INVALID),          # does not cover max_seq_len = 100
+    (2, 64, 7, 0, pda.PDA_ERR_INVALID),          # unknown variant
+    (2, 64, 1, 5, pda.PDA_ERR_INVALID),          # unknown merge mode
 ])
-def test_bad_plans_rejected(P, T, variant, status):
+def test_bad_plans_rejected(P, T, variant, merge, status):
     lib = pda.load_library()
     fake = ctypes.c_void_p(0x1000)
     s = _shape(max_seq_len=100, max_blocks_per_seq=7)
-    plan = pda.PdaPlan(num_partitions=P, tokens_per_partition=T, variant=variant, cu_count=1,
-                       workspace_bytes=0)
+    plan = pda.PdaPlan(num_partitions=P, tokens_per_partition=T, variant=variant, merge=merge,
+                       cu_count=1, workspace_bytes=0)
     rc = lib.paged_decode_attn_with_plan(ctypes.byref(s), ctypes.byref(plan), fake, fake, fake,
                                          fake, fake, 1.0, fake, fake, 1 << 30, None)
     assert rc == status

@@ -24,9 +24,9 @@ POISON = {"K": ("nan", "zero"), "V": ("zero", "nan"), "KV": ("nan", "nan"),
           "KV_1e4": ("1e4", "1e4")}
 
 
-def plan_of(P, T, variant=pda.PDA_VARIANT_VALU):
-    return pda.PdaPlan(num_partitions=P, tokens_per_partition=T, variant=variant, cu_count=0,
-                       workspace_bytes=0)
+def plan_of(P, T, variant=pda.PDA_VARIANT_VALU, merge=pda.PDA_MERGE_KERNEL):
+    return pda.PdaPlan(num_partitions=P, tokens_per_partition=T, variant=variant, merge=merge,
+                       cu_count=0, workspace_bytes=0)
 
 
 # ---- config 1: tiny paged GQA decode ------------------------------------
@@ -115,16 +115,54 @@ def test_group_and_head_sizes(D, G, dtype):
                                      seed=int(rng.integers(1 << 30)), tail_k="nan", tail_v="nan"))
     got = run(case)
     check(case, got, per_seq=True)
-    P, T = 5, 320  # forced multi-partition plan (some partitions empty)
-    got2 = run(case, plan=plan_of(P, T))
-    check(case, got2, per_seq=True)
+    P, T = 5, 320  # forced multi-partition plans (some partitions empty)
+    for merge in (pda.PDA_MERGE_FUSED, pda.PDA_MERGE_KERNEL):
+        got2 = run(case, plan=plan_of(P, T, merge=merge))
+        check(case, got2, per_seq=True)
+
+
+@pytest.mark.parametrize("mk", ["cfg4", "cfg5short"])
+def test_fused_and_kernel_merge_reuse_workspace(mk):
+    """Both merge paths agree with the oracle; the fused path's arrival
+    counters return to zero after every call, so one workspace serves a
+    sequence of calls (different plans included) with identical results."""
+    case = (configs.cfg4(16384, device="cuda") if mk == "cfg4"
+            else configs.cfg5(device="cuda", lo=1, hi=5000, cell=2))
+    shape = shape_of(case)
+    planned = pda.paged_decode_attn_plan(shape)
+    assert planned.merge == pda.PDA_MERGE_KERNEL and planned.num_partitions > 1
+    kplan = planned
+    planned = plan_of(planned.num_partitions, planned.tokens_per_partition,
+                      merge=pda.PDA_MERGE_FUSED)
+    ws = torch.empty(pda.pda_workspace_bytes(shape, planned), dtype=torch.uint8, device="cuda")
+    pda.paged_decode_attn_workspace_init(ws)
+    ref = reference(case)
+    first = None
+    for it in range(4):
+        plan = planned if it % 2 == 0 else kplan
+        out = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                    case.seq_lens_t, case.scale, workspace=ws,
+                                    max_seq_len=case.max_seq_len, plan=plan)
+        torch.cuda.synchronize()
+        check(case, out, ref, per_seq=True)
+        if plan is planned:
+            if first is None:
+                first = bits(out)
+            else:
+                assert np.array_equal(first, bits(out))
+    # the counters (last part of the workspace) are back at zero
+    nctr = case.B * case.Hkv
+    ctr_bytes = -(-(nctr * 4) // 256) * 256
+    ctr = ws[ws.numel() - ctr_bytes:].view(torch.int32)[:nctr]
+    assert int(ctr.abs().sum().item()) == 0
 
 
 def test_edge_lengths():
     lens = [0, 1, 2, 15, 16, 17, 63, 64, 65, 1000]
     case = to_device(kvgen.make_case(len(lens), 6, 2, 64, 16, lens, seed=77, tail_k="nan",
                                      tail_v="nan", max_blocks_per_seq=70))
-    for plan in (None, plan_of(1, 1024), plan_of(16, 64)):
+    for plan in (None, plan_of(1, 1024), plan_of(16, 64, merge=pda.PDA_MERGE_FUSED),
+                 plan_of(16, 64, merge=pda.PDA_MERGE_KERNEL)):
         got = run(case, plan=plan)
         g = got.float().cpu().numpy()
         assert np.all(g[0] == 0.0)                                  # L == 0 -> zeros
@@ -136,7 +174,8 @@ def test_edge_lengths():
 def test_empty_batch_rows_only():
     case = to_device(kvgen.make_case(2, 8, 4, 128, 16, [0, 0], seed=5, max_blocks_per_seq=2,
                                      max_seq_len=32))
-    for plan in (None, plan_of(1, 64), plan_of(3, 64)):
+    for plan in (None, plan_of(1, 64), plan_of(3, 64),
+                 plan_of(3, 64, merge=pda.PDA_MERGE_FUSED)):
         got = run(case, plan=plan)
         assert torch.all(got.float() == 0)
 
@@ -168,6 +207,9 @@ def test_forced_single_partition_vs_planned(mk):
     check(case, run(case), ref)
     T = -(-case.max_seq_len // 64) * 64
     check(case, run(case, plan=plan_of(1, T)), ref)
+    fplan = plan_of(planned.num_partitions, planned.tokens_per_partition,
+                    merge=pda.PDA_MERGE_FUSED)
+    check(case, run(case, plan=fplan), ref)
 
 
 # ---- bookkeeping: bit-exact against the oracle's recomputation ----------

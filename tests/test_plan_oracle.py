@@ -41,7 +41,7 @@ def test_plan_invariants(D):
 
 def test_workspace_bytes():
     assert plan.workspace_bytes(1, 32, 128, 1) == 0
-    assert plan.workspace_bytes(1, 24, 256, 128) == 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4
+    assert plan.workspace_bytes(1, 24, 256, 128, 4) == 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4 + 256
 
 
 def test_expected_trace_matches_token_loop():
