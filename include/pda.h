@@ -70,10 +70,10 @@ extern "C" {
 /* ---- kernel variants --------------------------------------------------- */
 /* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
  *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
- * PDA_VARIANT_MFMA: QK^T and PV on matrix-core tiles, the packed query group
- *   padded to 16 rows; reserved, not built in this version (a plan naming it
- *   is rejected with PDA_ERR_UNSUPPORTED).
- * The plan picks VALU. */
+ * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs) and PV on
+ *   v_mfma_f32_16x16x4_f32 (fp32 weights, exact fp32 V), the packed query
+ *   group padded to 16 rows; G <= PDA_MAX_GROUP.
+ * The plan picks VALU for G <= PDA_VALU_MAX_GROUP and MFMA above it. */
 #define PDA_VARIANT_VALU 1
 #define PDA_VARIANT_MFMA 2
 #define PDA_VALU_MAX_GROUP 8
@@ -207,14 +207,15 @@ int paged_decode_attn_timed(const pda_shape_t* shape, const pda_plan_t* plan,
                             void* start_event, void* stop_event, void* stream);
 
 /* Bookkeeping trace.  Runs the main kernel's own partitioning, tiling and
- * address generation (the same device functions) under `plan`, but instead of
- * loading K/V it records, for every token t the kernel consumes:
+ * address generation (the same device functions) under `plan` -- for the
+ * plan's variant, the rows its K loads (rows == 0) or its V loads (rows == 1)
+ * read -- but instead of loading K/V it records, for every token t consumed:
  *   trace_slot [B][Hkv][max_seq_len]  physical slot  block_id * bs + (t % bs)
  *   trace_part [B][Hkv][max_seq_len]  the partition p that consumed t
  * and for every unit trace_range [B][Hkv][P][2] = (t0, t1) (t1 <= t0 when the
  * partition is empty).  Entries for t >= seq_lens[b] are left untouched.
  * Device pointers; the caller pre-fills them with a sentinel. */
-int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan,
+int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan, int32_t rows,
                             const int32_t* block_table, const int32_t* seq_lens,
                             int32_t* trace_slot, int32_t* trace_part,
                             int32_t* trace_range, void* stream);

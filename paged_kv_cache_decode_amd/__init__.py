@@ -90,7 +90,7 @@ def load_library():
     lib.paged_decode_attn_timed.argtypes = [sp, pp, P, P, P, P, P, ctypes.c_float, P, P,
                                             ctypes.c_int64, P, P, P]
     lib.paged_decode_attn_timed.restype = ctypes.c_int
-    lib.paged_decode_attn_trace.argtypes = [sp, pp, P, P, P, P, P, P]
+    lib.paged_decode_attn_trace.argtypes = [sp, pp, ctypes.c_int32, P, P, P, P, P, P]
     lib.paged_decode_attn_trace.restype = ctypes.c_int
     lib.paged_decode_attn_workspace_init.argtypes = [P, ctypes.c_int64, P]
     lib.paged_decode_attn_workspace_init.restype = ctypes.c_int
@@ -266,8 +266,9 @@ def paged_decode_attn_timed(shape: PdaShape, plan: Optional[PdaPlan], q, k_cache
 
 
 def paged_decode_attn_trace(shape: PdaShape, plan: PdaPlan, block_table, seq_lens,
-                            stream=None, fill: int = -1):
-    """Run the bookkeeping trace; returns (slot [B,Hkv,Lmax], part [B,Hkv,Lmax],
+                            rows: int = 0, stream=None, fill: int = -1):
+    """Run the bookkeeping trace of the plan's variant (rows 0: the rows its K
+    loads read, 1: its V loads); returns (slot [B,Hkv,Lmax], part [B,Hkv,Lmax],
     ranges [B,Hkv,P,2]) as int32 device tensors pre-filled with `fill`."""
     import torch
     dev = block_table.device
@@ -276,7 +277,8 @@ def paged_decode_attn_trace(shape: PdaShape, plan: PdaPlan, block_table, seq_len
     part = torch.full_like(slot, fill)
     ranges = torch.full((B, Hkv, P, 2), fill, dtype=torch.int32, device=dev)
     rc = load_library().paged_decode_attn_trace(ctypes.byref(shape), ctypes.byref(plan),
-                                                _ptr(block_table), _ptr(seq_lens), _ptr(slot),
+                                                int(rows), _ptr(block_table), _ptr(seq_lens),
+                                                _ptr(slot),
                                                 _ptr(part), _ptr(ranges), _stream(stream))
     if rc != PDA_OK:
         raise PdaError(rc, "paged_decode_attn_trace")

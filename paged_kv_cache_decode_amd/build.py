@@ -30,6 +30,8 @@ def _units(csrc=CSRC):
         for hd in (64, 128, 256):
             units.append((os.path.join(csrc, "pda_decode_valu.hip"),
                           f"valu_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
+            units.append((os.path.join(csrc, "pda_decode_mfma.hip"),
+                          f"mfma_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
     units.append((os.path.join(csrc, "pda_merge.hip"), "merge.o", []))
     units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
     flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops"])

@@ -75,10 +75,19 @@ struct DecodeParams {
 };
 
 constexpr int kWave = 64;
-constexpr int kWaves = PDA_WAVES;
+// Wavefronts per workgroup of the decode kernels (tiles of a partition are
+// dealt to them round-robin).
+#ifndef PDA_KERNEL_WAVES
+#define PDA_KERNEL_WAVES 4
+#endif
+constexpr int kWaves = PDA_KERNEL_WAVES;
 constexpr int kTile = PDA_TILE;
 constexpr int kAlignTokens = 16;
 constexpr int kThreads = kWave * kWaves;
+
+// Heads are combined in chunks of at most this many through LDS at the end
+// of a unit.
+constexpr int kHeadChunk = 8;
 
 // Launchers (one translation unit per element type and head size).
 // `aligned` selects the path for block sizes that are multiples of the tile.
@@ -86,10 +95,19 @@ constexpr int kThreads = kWave * kWaves;
 hipError_t launch_decode_valu(int dtype, int head_size, int group_pad, bool aligned,
                               const DecodeParams& p, int batch, hipStream_t stream,
                               hipEvent_t start, hipEvent_t stop);
+hipError_t launch_decode_mfma(int dtype, int head_size, bool aligned, const DecodeParams& p,
+                              int batch, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(int dtype, int head_size, const DecodeParams& p, int batch,
                         hipStream_t stream);
-hipError_t launch_trace(int head_size, bool aligned, const DecodeParams& p, int batch,
+// rows: 0 = the VALU kernel's rows, 1 = the MFMA kernel's K rows, 2 = its V rows
+hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
                         hipStream_t stream);
+
+// Bytes of dynamic LDS the MFMA kernel uses (head chunks of kHeadChunk).
+inline size_t mfma_lds_bytes(int head_size, int tbl_capacity) {
+    return (size_t)kWaves * kHeadChunk * (head_size + 2) * sizeof(float) +
+           (size_t)tbl_capacity * sizeof(int32_t);
+}
 
 // Padded group sizes the VALU kernel is compiled for.
 inline int valu_group_pad(int g) {

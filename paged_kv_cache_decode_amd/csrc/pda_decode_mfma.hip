@@ -1,0 +1,274 @@
+// Paged-attention decode, matrix-core variant, for gfx950.
+//
+// Same unit of work as the VALU variant -- one workgroup of 4 wavefronts per
+// (partition p, KV head g, sequence b), all G query heads of the group packed,
+// every K/V byte read once -- but both contractions run on MFMA, with the
+// packed group padded to 16 rows:
+//
+//   QK^T  S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: a 16-token tile of K
+//         rows is the A operand (lane l loads 16 bytes of token l%16), Q^T the
+//         B operand.  The 16x16 result leaves each lane the scores of one
+//         head (l%16) for four tokens (4(l/16) + r, r = 0..3).
+//   mask  scores of tokens at or past the partition end become -inf by select;
+//         tail slots are never addressed (see locate_row).
+//   softmax  online, exp2 domain; the running max per head is shared by the
+//         four lanes that hold that head; the accumulator is rescaled only
+//         when some max grew.
+//   PV    O = P V on v_mfma_f32_16x16x4_f32: the exp'd scores are already in
+//         the A-operand layout (row = head l%16, k = token 4(l/16) + r), and
+//         round r of V loads token 4(l/16) + r, 16 bytes per lane, so each of
+//         the lane's 8 elements is the B operand of one MFMA.  V never needs
+//         a transpose; P stays fp32 (no rounding of the weights to 16 bits).
+//
+// VALU work per tile is reduced to the 16-bit -> fp32 conversion of V and the
+// softmax bookkeeping, independent of G.
+//
+// Compiled once per (element type, head size): PDA_DTYPE (0 bf16, 1 fp16)
+// and PDA_HEAD (64, 128, 256).
+#include <hip/hip_ext.h>
+
+#include "pda_device.h"
+
+#ifndef PDA_DTYPE
+#error "PDA_DTYPE must be defined"
+#endif
+#ifndef PDA_HEAD
+#error "PDA_HEAD must be defined"
+#endif
+
+namespace pda {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename Elt>
+struct MfmaQK;
+template <>
+struct MfmaQK<BF16> {
+    __device__ static inline f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaQK<FP16> {
+    __device__ static inline f32x4_t run(uint4 a, uint4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+};
+
+// The element type and head size are template parameters of the kernel so
+// that every instantiation has its own symbol across translation units.
+template <typename Elt, int D, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+    using Geo = MfmaGeom<D>;
+    constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
+    extern __shared__ float smem[];
+    float* red = smem;                                                       // [kWaves][8][D+2]
+    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * kHeadChunk * (D + 2));
+
+    const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int q4 = lane >> 4, c16 = lane & 15;
+    const int G = p.group;
+    const int L = context_len(p, b);
+    const int t0 = part * p.tokens_per_part;
+    const bool direct = p.num_partitions == 1;
+
+    if (t0 >= L) {  // empty partition; the first one of an empty context writes zeros
+        if (part == 0) zero_unit_rows<D>(p, b, g);
+        return;
+    }
+    const int t1 = min(t0 + p.tokens_per_part, L);
+    const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
+    const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
+    stage_table_slice(p, b, lb0, lb1, tbl);
+
+    // Q^T as the B operand: head c16 of the group (zero rows past G),
+    // elements 32s + 8*q4 .. +8 for k-step s
+    uint4 qb[KS];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                               ((int64_t)b * p.num_q_heads + g * G + c16) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qb[s] = (c16 < G) ? *reinterpret_cast<const uint4*>(qrow + 32 * s)
+                              : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    const char* kc = static_cast<const char*>(p.k_cache);
+    const char* vc = static_cast<const char*>(p.v_cache);
+    const int64_t head_off = (int64_t)g * p.head_stride;               // elements
+    const uint32_t k_lane = (uint32_t)(8 * q4) * 2;                     // bytes
+    const uint32_t v_lane = (uint32_t)(8 * (c16 % CW)) * 2;             // bytes
+    const int ntiles = (t1 - t0 + TT - 1) / TT;
+
+    auto load_tile = [&](int j, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
+        const int tile_base = t0 + j * TT;
+        int phys, slot0, dt;
+        locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, mfma_k_offset(lane), phys, slot0, dt);
+        {
+            const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+            const uint32_t off = (uint32_t)dt * (2 * D) + k_lane;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kr[s] = load_row16(kc + base + off + 64 * s);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, mfma_v_offset(lane, r), phys, slot0,
+                                dt);
+            const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+            const uint32_t off = (uint32_t)dt * (2 * D) + v_lane;
+#pragma unroll
+            for (int dh = 0; dh < DH; ++dh) vr[r][dh] = load_row16(vc + base + off + 256 * dh);
+        }
+    };
+
+    f32x4_t oacc[DH][8];
+#pragma unroll
+    for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -FLT_MAX;  // running max of head c16 (finite floor: exp2(-inf - m) = 0)
+    float l = 0.f;       // this lane's share of head c16's denominator
+
+    auto process = [&](int j, const uint4 (&kr)[KS], const uint4 (&vr)[4][DH]) {
+        const int tile_base = t0 + j * TT;
+        const bool full = tile_base + TT <= t1;
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(kr[s], qb[s], sacc);
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * p.scale_log2;
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sc[r] = tile_base + mfma_v_offset(lane, r) < t1 ? sc[r] : -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        if (__builtin_amdgcn_ballot_w64(mn > m)) {
+            const float alpha = fast_exp2(m - mn);
+            l *= alpha;
+            // the accumulator rows of this lane are heads 4*q4 + r
+            float ar[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+            for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) oacc[dh][e][r] *= ar[r];
+            m = mn;
+        }
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(sc[r] - m);
+            l += pr[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int dh = 0; dh < DH; ++dh) {
+                const uint4 w = vr[r][dh];
+                float vf[8];
+                vf[0] = Elt::lo(w.x); vf[1] = Elt::hi(w.x);
+                vf[2] = Elt::lo(w.y); vf[3] = Elt::hi(w.y);
+                vf[4] = Elt::lo(w.z); vf[5] = Elt::hi(w.z);
+                vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    oacc[dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vf[e], oacc[dh][e],
+                                                                      0, 0, 0);
+            }
+        }
+    };
+
+    // Two register buffers, loop rotated so that its head waits for buffer a
+    // while buffer b is in flight (see the VALU variant).
+    const auto clampt = [&](int jj) { return min(jj, ntiles - 1); };
+    int j = wave;
+    uint4 ka[KS], va[4][DH], kb[KS], vb[4][DH];
+    if (j < ntiles) {
+        load_tile(j, ka, va);
+        load_tile(clampt(j + kWaves), kb, vb);
+    }
+    for (; j < ntiles; j += 2 * kWaves) {
+        process(j, ka, va);
+        if (j + kWaves >= ntiles) break;
+        load_tile(clampt(j + 2 * kWaves), ka, va);
+        process(j + kWaves, kb, vb);
+        load_tile(clampt(j + 3 * kWaves), kb, vb);
+    }
+
+    // full denominator of head c16 (all four lane groups hold the same m)
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+
+    // merge the wavefronts and write the unit's result, heads in chunks
+    for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
+        const int hn = min(kHeadChunk, G - h0);
+        if (c16 < CW) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hi = 4 * q4 + r - h0;
+                if (hi < 0 || hi >= hn) continue;
+                float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+#pragma unroll
+                for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) row[dh * 128 + 8 * c16 + e] = oacc[dh][e][r];
+            }
+        }
+        if (q4 == 0 && c16 >= h0 && c16 < h0 + hn) {
+            float* row = red + (wave * kHeadChunk + c16 - h0) * (D + 2);
+            row[D] = m;
+            row[D + 1] = l;
+        }
+        __syncthreads();
+        write_unit_rows<Elt, D>(p, red, kHeadChunk, h0, hn, b, g, part);
+        __syncthreads();
+    }
+    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, L, b, g);
+}
+
+#if PDA_DTYPE == 0
+using EltT = BF16;
+#else
+using EltT = FP16;
+#endif
+constexpr int kHead = PDA_HEAD;
+
+template <bool ALIGNED>
+static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+    const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
+    const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
+    if (start || stop)
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED>), grid, dim3(kThreads), lds,
+                              stream, start, stop, 0, p);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED>), grid, dim3(kThreads), lds,
+                           stream, p);
+    return hipGetLastError();
+}
+
+#define PDA_CAT2(a, b, c) a##_##b##_##c
+#define PDA_CAT(a, b, c) PDA_CAT2(a, b, c)
+hipError_t PDA_CAT(launch_decode_mfma, PDA_DTYPE, PDA_HEAD)(bool aligned, const DecodeParams& p,
+                                                            int batch, hipStream_t stream,
+                                                            hipEvent_t e0, hipEvent_t e1) {
+    return aligned ? launch_one<true>(p, batch, stream, e0, e1)
+                   : launch_one<false>(p, batch, stream, e0, e1);
+}
+
+}  // namespace pda

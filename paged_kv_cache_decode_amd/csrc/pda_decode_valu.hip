@@ -33,8 +33,9 @@
 #error "PDA_HEAD must be defined"
 #endif
 
+// Tiles in flight per wave (register buffers in rotation): 3 measured best.
 #ifndef PDA_VALU_STAGES
-#define PDA_VALU_STAGES 2
+#define PDA_VALU_STAGES 3
 #endif
 #if PDA_VALU_SCHED_FENCE
 #define PDA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -43,35 +44,6 @@
 #endif
 
 namespace pda {
-
-// Log-sum-exp merge of the Pb partials (o_p normalised, m_p, l_p in the exp2
-// domain) of the G heads of unit (b, g), one output element per thread and
-// step, partitions in index order with a running max:
-//   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p.
-template <typename Elt, int D>
-__device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
-    uint16_t* out16 = static_cast<uint16_t*>(p.out);
-    const int G = p.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int i = idx / D, d = idx - i * D;
-        const int64_t row = (int64_t)b * p.num_q_heads + g * G + i;
-        const float* ml = p.ws_ml + row * p.num_partitions * 2;
-        const float* po = p.ws_o + row * p.num_partitions * D + d;
-        float M = -FLT_MAX, o = 0.f, den = 0.f;
-#pragma unroll 8
-        for (int q = 0; q < Pb; ++q) {
-            const float2 mlq = make_float2(load_coherent(ml + 2 * q), load_coherent(ml + 2 * q + 1));
-            const float oq = load_coherent(po + (int64_t)q * D);
-            const float mn = fmaxf(M, mlq.x);
-            const float sc = fast_exp2(M - mn);
-            const float w = mlq.y * fast_exp2(mlq.x - mn);
-            o = o * sc + w * oq;
-            den = den * sc + w;
-            M = mn;
-        }
-        out16[row * D + d] = Elt::from_float(o / den);
-    }
-}
 
 // The element type and head size are template parameters of the kernel (not
 // only of this translation unit) so that every instantiation has its own
@@ -92,12 +64,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int L = context_len(p, b);
     const int t0 = part * p.tokens_per_part;
     const bool direct = p.num_partitions == 1;
-    uint16_t* out16 = static_cast<uint16_t*>(p.out);
 
     if (t0 >= L) {  // empty partition; the first one of an empty context writes zeros
-        if (part == 0)
-            for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
-                out16[((int64_t)b * p.num_q_heads + g * G) * D + idx] = 0;
+        if (part == 0) zero_unit_rows<D>(p, b, g);
         return;
     }
     const int t1 = min(t0 + p.tokens_per_part, L);
@@ -284,59 +253,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     __syncthreads();
 
     // merge the wavefronts and write the unit's result
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int i = idx / D, d = idx - i * D;
-        float M = -FLT_MAX;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * GP + i) * (D + 2) + D]);
-        float o = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float* row = red + (w * GP + i) * (D + 2);
-            const float wt = fast_exp2(row[D] - M);
-            den += row[D + 1] * wt;
-            o += row[d] * wt;
-        }
-        const int h = g * G + i;
-        if (direct) {
-            out16[((int64_t)b * p.num_q_heads + h) * D + d] = Elt::from_float(o / den);
-        } else {
-            const int64_t prow = ((int64_t)b * p.num_q_heads + h) * p.num_partitions + part;
-            if (p.fused_merge) {  // read back by another workgroup of this launch
-                store_coherent(p.ws_o + prow * D + d, o / den);
-                if (d == 0) {
-                    store_coherent(p.ws_ml + prow * 2, M);
-                    store_coherent(p.ws_ml + prow * 2 + 1, den);
-                }
-            } else {              // read by the merge kernel after this launch
-                p.ws_o[prow * D + d] = o / den;
-                if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
-            }
-        }
-    }
-    if (direct || !p.fused_merge) return;
-
-    // Fused split-KV merge: the unit that finishes last among the Pb non-empty
-    // partitions of (b, g) merges them.  The partials above were stored at
-    // device scope (write-through to the point where all XCDs see them); each
-    // wave waits for its stores to be acknowledged before the workgroup
-    // barrier, then thread 0 counts the arrival with a device-scope atomic.
-    // The last arrival resets the counter for the next call and reads the
-    // partials back with device-scope loads.  No L2 write-back or invalidate
-    // is needed.
-    __shared__ int s_last;
-    wait_stores_done();
-    __syncthreads();
-    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
-    if (threadIdx.x == 0) {
-        int32_t* ctr = p.counters + (int64_t)b * p.num_kv_heads + g;
-        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == Pb - 1;
-        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    merge_unit<Elt, D>(p, b, g, Pb);
+    write_unit_rows<Elt, D>(p, red, GP, 0, G, b, g, part);
+    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, L, b, g);
 }
 
 #if PDA_DTYPE == 0

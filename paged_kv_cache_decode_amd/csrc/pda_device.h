@@ -151,26 +151,27 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
     return max(0, min(p.seq_lens[b], p.max_seq_len));
 }
 
-// Physical block and slot of the token that round u, lane-row r of the tile
-// starting at tile_base reads: slot = slot0 + dt.  Tokens at or past t1 (the
-// partition end, never past the sequence end) are redirected to token t1-1,
-// so no slot at or past seq_len is ever addressed.  Block ids are clamped
-// into the pool, so a corrupt table entry gives a wrong row, never an access
-// outside the pool.
-//  ALIGNED (block size a multiple of 16): the round's tokens lie in one block
-//  (R divides 16 and rounds start at multiples of R), located once per round
-//  from the round's first (clamped) token: phys and slot0 are wave-uniform,
-//  dt in [0, R) is the lane's row offset.
+// Physical block and slot of the row a lane reads: the token at in-tile
+// offset `o` of the tile starting at tile_base, slot = slot0 + dt.  Tokens at
+// or past t1 (the partition end, never past the sequence end) are redirected
+// to token t1-1, so no slot at or past seq_len is ever addressed.  Block ids
+// are clamped into the pool, so a corrupt table entry gives a wrong row,
+// never an access outside the pool.
+//  ALIGNED (block size a multiple of 16, tiles starting at multiples of 16
+//  tokens or of the round length): all offsets a wave reads together lie in
+//  the 16-token group that contains offset o0 (wave-uniform), which lies in
+//  one block; phys and slot0 are located once from o0 and are wave-uniform,
+//  dt is the lane's row offset.
 //  Otherwise every lane divides its own token index by the block size and
 //  dt = 0.
-template <int R, bool ALIGNED>
-__device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, int lb0,
-                                    int tile_base, int t1, int u, int r, int& phys, int& slot0,
-                                    int& dt) {
+template <bool ALIGNED>
+__device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int lb0,
+                                  int tile_base, int t1, int o0, int o, int& phys, int& slot0,
+                                  int& dt) {
     const int last = t1 - 1 - tile_base;
-    const int t = tile_base + min(u * R + r, last);
+    const int t = tile_base + min(o, last);
     if constexpr (ALIGNED) {
-        const int ub = tile_base + min(u * R, last);
+        const int ub = tile_base + min(o0, last);
         const int lb = (int)fastdiv((uint32_t)ub, p.bs_div);
         slot0 = ub - lb * p.block_size;
         dt = t - ub;
@@ -182,6 +183,133 @@ __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, i
         dt = 0;
         phys = min(max(tbl[lb - lb0], 0), p.num_blocks - 1);
     }
+}
+
+// The VALU kernel's rows: round u of a tile, lane-row r (R rows per round;
+// R divides 16 and rounds start at multiples of R).
+template <int R, bool ALIGNED>
+__device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, int lb0,
+                                    int tile_base, int t1, int u, int r, int& phys, int& slot0,
+                                    int& dt) {
+    locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, u * R, u * R + r, phys, slot0, dt);
+}
+
+// ---- MFMA tile geometry --------------------------------------------------
+// A 16-token tile.  K rows feed the A operand of v_mfma_f32_16x16x32 (S^T =
+// K Q^T): lane l reads token l%16, elements 32s + 8(l/16) .. +8 for k-step s.
+// V rows feed the B operand of v_mfma_f32_16x16x4_f32 (O^T... O = P V): for
+// round r lane l reads token 4(l/16) + r, elements dh*128 + 8*(l%16 % CW) .. +8,
+// CW = min(16, D/8) column groups per 128-wide half dh.
+template <int D>
+struct MfmaGeom {
+    static constexpr int KS = D / 32;                 // QK k-steps (16-byte K loads per tile)
+    static constexpr int DH = D >= 128 ? D / 128 : 1; // 128-wide halves of V
+    static constexpr int CW = D >= 128 ? 16 : D / 8;  // distinct column groups per half
+};
+__device__ inline int mfma_k_offset(int lane) { return lane & 15; }
+__device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + r; }
+
+
+// ---- unit epilogue shared by the decode kernels ------------------------
+// Combine the kWaves per-wave states of heads h0 .. h0+hn-1 of unit (b, g),
+// staged in LDS as red[w][i][0..D) = unnormalised O, red[w][i][D] = running
+// max m (exp2 domain), red[w][i][D+1] = denominator l, in a fixed order, and
+// write either the 16-bit output (one partition) or the fp32 partial.
+template <typename Elt, int D>
+__device__ inline void write_unit_rows(const DecodeParams& p, const float* red, int red_heads,
+                                       int h0, int hn, int b, int g, int part) {
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+    const bool direct = p.num_partitions == 1;
+    for (int idx = threadIdx.x; idx < hn * D; idx += blockDim.x) {
+        const int i = idx / D, d = idx - i * D;
+        float M = -FLT_MAX;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * red_heads + i) * (D + 2) + D]);
+        float o = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float* row = red + (w * red_heads + i) * (D + 2);
+            const float wt = fast_exp2(row[D] - M);
+            den += row[D + 1] * wt;
+            o += row[d] * wt;
+        }
+        const int h = g * p.group + h0 + i;
+        if (direct) {
+            out16[((int64_t)b * p.num_q_heads + h) * D + d] = Elt::from_float(o / den);
+        } else {
+            const int64_t prow = ((int64_t)b * p.num_q_heads + h) * p.num_partitions + part;
+            if (p.fused_merge) {  // read back by another workgroup of this launch
+                store_coherent(p.ws_o + prow * D + d, o / den);
+                if (d == 0) {
+                    store_coherent(p.ws_ml + prow * 2, M);
+                    store_coherent(p.ws_ml + prow * 2 + 1, den);
+                }
+            } else {              // read by the merge kernel after this launch
+                p.ws_o[prow * D + d] = o / den;
+                if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge of the Pb partials (o_p normalised, m_p, l_p in the exp2
+// domain) of the G heads of unit (b, g), one output element per thread and
+// step, partitions in index order with a running max:
+//   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p.
+template <typename Elt, int D>
+__device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+    const int G = p.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+        const int i = idx / D, d = idx - i * D;
+        const int64_t row = (int64_t)b * p.num_q_heads + g * G + i;
+        const float* ml = p.ws_ml + row * p.num_partitions * 2;
+        const float* po = p.ws_o + row * p.num_partitions * D + d;
+        float M = -FLT_MAX, o = 0.f, den = 0.f;
+#pragma unroll 8
+        for (int q = 0; q < Pb; ++q) {
+            const float mq = load_coherent(ml + 2 * q), lq = load_coherent(ml + 2 * q + 1);
+            const float oq = load_coherent(po + (int64_t)q * D);
+            const float mn = fmaxf(M, mq);
+            const float sc = fast_exp2(M - mn);
+            const float w = lq * fast_exp2(mq - mn);
+            o = o * sc + w * oq;
+            den = den * sc + w;
+            M = mn;
+        }
+        out16[row * D + d] = Elt::from_float(o / den);
+    }
+}
+
+// Fused split-KV merge: the unit that finishes last among the Pb non-empty
+// partitions of (b, g) merges them.  The partials were stored at device scope
+// (write-through to the point where all XCDs see them); each wave waits for
+// its stores to be acknowledged before the workgroup barrier, then thread 0
+// counts the arrival with a device-scope atomic.  The last arrival resets the
+// counter for the next call and reads the partials back with device-scope
+// loads.  No L2 write-back or invalidate is needed.
+template <typename Elt, int D>
+__device__ inline void fused_merge_tail(const DecodeParams& p, int L, int b, int g) {
+    __shared__ int s_last;
+    wait_stores_done();
+    __syncthreads();
+    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
+    if (threadIdx.x == 0) {
+        int32_t* ctr = p.counters + (int64_t)b * p.num_kv_heads + g;
+        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == Pb - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_last) merge_unit<Elt, D>(p, b, g, Pb);
+}
+
+// Zero output rows of the G heads of (b, g) (an empty context).
+template <int D>
+__device__ inline void zero_unit_rows(const DecodeParams& p, int b, int g) {
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+    for (int idx = threadIdx.x; idx < p.group * D; idx += blockDim.x)
+        out16[((int64_t)b * p.num_q_heads + g * p.group) * D + idx] = 0;
 }
 
 }  // namespace pda

@@ -20,6 +20,33 @@ hipError_t launch_decode_valu_1_128(int, bool, const DecodeParams&, int, hipStre
 hipError_t launch_decode_valu_1_256(int, bool, const DecodeParams&, int, hipStream_t,
                                        hipEvent_t, hipEvent_t);
 
+hipError_t launch_decode_mfma_0_64(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+hipError_t launch_decode_mfma_0_128(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+hipError_t launch_decode_mfma_0_256(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+hipError_t launch_decode_mfma_1_64(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+hipError_t launch_decode_mfma_1_128(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+hipError_t launch_decode_mfma_1_256(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                       hipEvent_t);
+
+hipError_t launch_decode_mfma(int dtype, int head_size, bool aligned, const DecodeParams& p,
+                              int batch, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (dtype == PDA_BF16) {
+        if (head_size == 64) return launch_decode_mfma_0_64(aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_mfma_0_128(aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_mfma_0_256(aligned, p, batch, s, e0, e1);
+    } else {
+        if (head_size == 64) return launch_decode_mfma_1_64(aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_mfma_1_128(aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_mfma_1_256(aligned, p, batch, s, e0, e1);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode_valu(int dtype, int head_size, int gpad, bool aligned,
                               const DecodeParams& p, int batch, hipStream_t s, hipEvent_t e0,
                               hipEvent_t e1) {
@@ -73,7 +100,8 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
                                                       (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else if (pl->variant == PDA_VARIANT_MFMA) {
-        return PDA_ERR_UNSUPPORTED;  // not built in this library version
+        const int64_t lds = (int64_t)mfma_lds_bytes(s->head_size, (int)table_capacity(s, pl));
+        if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else {
         return PDA_ERR_INVALID;
     }
@@ -167,7 +195,8 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     if (P < 1) P = 1;
     plan->num_partitions = (int32_t)P;
     plan->tokens_per_partition = (int32_t)tp;
-    plan->variant = PDA_VARIANT_VALU;
+    plan->variant = s->num_q_heads / s->num_kv_heads > kValuMaxGroup ? PDA_VARIANT_MFMA
+                                                                      : PDA_VARIANT_VALU;
     plan->merge = PDA_MERGE_KERNEL;
     plan->cu_count = cu_count;
     plan->workspace_bytes = pda_workspace_bytes(s, plan);
@@ -238,8 +267,11 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int G = p.group;
     const bool aligned = block_aligned(s);
-    hipError_t e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(G), aligned, p,
-                                      s->num_seqs, st, ev0, ev1);
+    hipError_t e = pl->variant == PDA_VARIANT_MFMA
+                       ? launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
+                                            ev0, ev1)
+                       : launch_decode_valu(s->dtype, s->head_size, valu_group_pad(G), aligned, p,
+                                            s->num_seqs, st, ev0, ev1);
     if (e != hipSuccess) return PDA_ERR_LAUNCH;
     if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
         e = launch_merge(s->dtype, s->head_size, p, s->num_seqs, st);
@@ -287,7 +319,7 @@ int paged_decode_attn(const pda_shape_t* s, const void* q, const void* k_cache,
                                        out, workspace, workspace_bytes, stream);
 }
 
-int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl,
+int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl, int32_t rows,
                             const int32_t* block_table, const int32_t* seq_lens,
                             int32_t* trace_slot, int32_t* trace_part, int32_t* trace_range,
                             void* stream) {
@@ -297,6 +329,8 @@ int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl,
     if (rc != PDA_OK) return rc;
     if (!block_table || !seq_lens || !trace_slot || !trace_part || !trace_range)
         return PDA_ERR_INVALID;
+    if (rows != 0 && rows != 1) return PDA_ERR_INVALID;
+    const int pattern = pl->variant == PDA_VARIANT_MFMA ? 1 + rows : 0;
     DecodeParams p = make_params(s, pl, 1.0f);
     p.block_table = block_table;
     p.seq_lens = seq_lens;
@@ -304,7 +338,7 @@ int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl,
     p.trace_part = trace_part;
     p.trace_range = trace_range;
     const bool aligned = block_aligned(s);
-    hipError_t e = launch_trace(s->head_size, aligned, p, s->num_seqs,
+    hipError_t e = launch_trace(s->head_size, aligned, pattern, p, s->num_seqs,
                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
 }
@@ -325,7 +359,7 @@ const char* pda_status_string(int status) {
 #define PDA_BUILD_FLAGS "unknown"
 #endif
 const char* pda_build_id(void) {
-    return "libpda 0.2.0; target gfx950; variants valu; merge fused|kernel; flags " PDA_BUILD_FLAGS;
+    return "libpda 0.2.0; target gfx950; variants valu|mfma; merge fused|kernel; flags " PDA_BUILD_FLAGS;
 }
 
 }  // extern "C"

@@ -1,18 +1,22 @@
 // Bookkeeping trace of the paged decode, for gfx950.
 //
-// Same grid, partition bounds, table staging, tile walk and token location
-// (ValuGeom, stage_table_slice, locate_token) as the decode kernel, but each
-// lane that would load a token row records which physical slot and which
-// partition it used, instead of loading it.  Tests compare the trace bit for
-// bit with a recomputation from the definition of the paged cache.
+// Same grid, partition bounds, table staging, tile walk and row location
+// (stage_table_slice, locate_token / locate_row and the lane-to-row maps of
+// ValuGeom and MfmaGeom) as the decode kernels, but each lane that would load
+// a token row records which physical slot and which partition it used,
+// instead of loading it.  ROWS selects whose rows: 0 the VALU kernel's (K and
+// V alike), 1 the MFMA kernel's K rows, 2 its V rows.  Tests compare the
+// trace bit for bit with a recomputation from the definition of the paged
+// cache.
 #include "pda_device.h"
 
 namespace pda {
 
-template <int D, bool ALIGNED>
+template <int D, bool ALIGNED, int ROWS>
 __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     using Geo = ValuGeom<D>;
-    constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U, TT = Geo::TT;
+    constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U;
+    constexpr int TT = ROWS == 0 ? Geo::TT : 16;
     extern __shared__ int32_t tbl[];
     const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
@@ -32,39 +36,63 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     stage_table_slice(p, b, lb0, lb1, tbl);
     __syncthreads();
     const int ntiles = (t1 - t0 + TT - 1) / TT;
+    auto record = [&](int t, int phys, int slot) {
+        const int64_t at = unit * p.max_seq_len + t;
+        p.trace_slot[at] = phys * p.block_size + slot;
+        p.trace_part[at] = part;
+    };
     for (int j = wave; j < ntiles; j += kWaves) {
         const int tile_base = t0 + j * TT;
+        int phys, slot0, dt;
+        if constexpr (ROWS == 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int phys, slot0, dt;
-            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
-            const int t = tile_base + u * R + r;
-            if (c == 0 && t < t1) {
-                const int64_t at = unit * p.max_seq_len + t;
-                p.trace_slot[at] = phys * p.block_size + slot0 + dt;
-                p.trace_part[at] = part;
+            for (int u = 0; u < U; ++u) {
+                locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
+                const int t = tile_base + u * R + r;
+                if (c == 0 && t < t1) record(t, phys, slot0 + dt);
+            }
+        } else if constexpr (ROWS == 1) {
+            const int o = mfma_k_offset(lane);
+            locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, o, phys, slot0, dt);
+            if ((lane >> 4) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int o = mfma_v_offset(lane, rr);
+                locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, o, phys, slot0, dt);
+                if ((lane & 15) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
             }
         }
     }
 }
 
-template <int D, bool ALIGNED>
+template <int D, bool ALIGNED, int ROWS>
 static hipError_t launch_trace_t(const DecodeParams& p, int batch, hipStream_t stream) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
-    hipLaunchKernelGGL((trace_kernel<D, ALIGNED>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((trace_kernel<D, ALIGNED, ROWS>), grid, dim3(kThreads),
                        (size_t)p.tbl_capacity * sizeof(int32_t), stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_trace(int head_size, bool aligned, const DecodeParams& p, int batch,
+template <int D>
+static hipError_t launch_trace_d(bool aligned, int rows, const DecodeParams& p, int batch,
+                                 hipStream_t s) {
+    if (aligned) {
+        if (rows == 0) return launch_trace_t<D, true, 0>(p, batch, s);
+        if (rows == 1) return launch_trace_t<D, true, 1>(p, batch, s);
+        return launch_trace_t<D, true, 2>(p, batch, s);
+    }
+    if (rows == 0) return launch_trace_t<D, false, 0>(p, batch, s);
+    if (rows == 1) return launch_trace_t<D, false, 1>(p, batch, s);
+    return launch_trace_t<D, false, 2>(p, batch, s);
+}
+
+hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
                         hipStream_t stream) {
     switch (head_size) {
-        case 64: return aligned ? launch_trace_t<64, true>(p, batch, stream)
-                                : launch_trace_t<64, false>(p, batch, stream);
-        case 128: return aligned ? launch_trace_t<128, true>(p, batch, stream)
-                                 : launch_trace_t<128, false>(p, batch, stream);
-        case 256: return aligned ? launch_trace_t<256, true>(p, batch, stream)
-                                 : launch_trace_t<256, false>(p, batch, stream);
+        case 64: return launch_trace_d<64>(aligned, rows, p, batch, stream);
+        case 128: return launch_trace_d<128>(aligned, rows, p, batch, stream);
+        case 256: return launch_trace_d<256>(aligned, rows, p, batch, stream);
     }
     return hipErrorInvalidValue;
 }

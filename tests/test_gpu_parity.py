@@ -29,6 +29,19 @@ def plan_of(P, T, variant=pda.PDA_VARIANT_VALU, merge=pda.PDA_MERGE_KERNEL):
                        cu_count=0, workspace_bytes=0)
 
 
+VARIANTS = {"valu": pda.PDA_VARIANT_VALU, "mfma": pda.PDA_VARIANT_MFMA}
+
+
+def device_plan(case, variant=None, merge=None):
+    """The device's own plan, optionally with the variant / merge overridden."""
+    plan = pda.paged_decode_attn_plan(shape_of(case))
+    if variant is not None:
+        plan.variant = VARIANTS[variant]
+    if merge is not None:
+        plan.merge = merge
+    return plan
+
+
 # ---- config 1: tiny paged GQA decode ------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_cfg1_tiny(dtype):
@@ -48,15 +61,17 @@ def test_cfg2_sweep(hq, L):
 
 
 # ---- config 3: gemma-like layer, straddling lengths, NaN tails -----------
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("L", configs.CFG3_LENS)
-def test_cfg3_b1_fault_matrix(dtype, L):
+def test_cfg3_b1_fault_matrix(dtype, L, variant):
     clean = configs.cfg3(1, L, dtype=dtype, device="cuda", tail_k="zero", tail_v="zero")
-    ref_out = run(clean)
+    plan = device_plan(clean, variant)
+    ref_out = run(clean, plan=plan)
     check(clean, ref_out)
     for mode, (tk, tv) in POISON.items():
         poisoned = kvgen.page(clean, tk, tv)
-        got = run(poisoned)
+        got = run(poisoned, plan=plan)
         assert np.array_equal(bits(got), bits(ref_out)), f"{mode} tail changed the output"
 
 
@@ -99,6 +114,45 @@ def test_cfg5_mixed_batch_short(dtype):
     check(case, got, per_seq=True)
     clean = kvgen.page(case, "zero", "zero")
     assert np.array_equal(bits(got), bits(run(clean)))
+
+
+# ---- the MFMA variant over the whole shape space ------------------------
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8, 11, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_mfma_variant(D, G, dtype):
+    rng = np.random.default_rng(D * 77 + G + (500 if dtype == "fp16" else 0))
+    B = 3
+    Hkv = int(rng.integers(1, 3))
+    bs = int(rng.choice([1, 5, 16, 48, 784]))
+    lens = [int(x) for x in rng.integers(1, 1500, size=B)]
+    case = to_device(kvgen.make_case(B, G * Hkv, Hkv, D, bs, lens, dtype=dtype,
+                                     seed=int(rng.integers(1 << 30)), tail_k="nan", tail_v="nan"))
+    ref = reference(case)
+    for plan in (device_plan(case, "mfma"),
+                 plan_of(5, 320, variant=pda.PDA_VARIANT_MFMA),
+                 plan_of(5, 320, variant=pda.PDA_VARIANT_MFMA, merge=pda.PDA_MERGE_FUSED),
+                 plan_of(1, 1536, variant=pda.PDA_VARIANT_MFMA)):
+        check(case, run(case, plan=plan), ref, per_seq=True)
+
+
+@pytest.mark.parametrize("mk", ["cfg4-32K", "cfg2-32K", "cfg5"])
+def test_mfma_variant_full_size(mk):
+    case = {"cfg4-32K": lambda: configs.cfg4(32768, device="cuda"),
+            "cfg2-32K": lambda: configs.cfg2(32, 32768, device="cuda"),
+            "cfg5": lambda: configs.cfg5(device="cuda")}[mk]()
+    got = run(case, plan=device_plan(case, "mfma"))
+    seqs = [0] if case.B == 1 else [0, 9, 33, 63]
+    check(case, got, seqs=seqs, per_seq=True)
+
+
+def test_mfma_matches_valu_closely():
+    """Two implementations of the same sums: both within tolerance of the
+    oracle and close to each other (fp32 accumulation order only)."""
+    case = configs.cfg4(24576, device="cuda")
+    a = run(case, plan=device_plan(case, "valu")).float()
+    b = run(case, plan=device_plan(case, "mfma")).float()
+    assert float((a - b).abs().max()) <= 2 * 2.0 ** -8 * float(a.abs().max())
 
 
 # ---- the whole space of shapes at small sizes -------------------------
@@ -181,21 +235,25 @@ def test_empty_batch_rows_only():
 
 
 # ---- invariants --------------------------------------------------------
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("bs", [16, 784, 5])
-def test_block_permutation_bit_identical(bs):
+def test_block_permutation_bit_identical(bs, variant):
     case = to_device(kvgen.make_case(4, 24, 4, 256 if bs == 784 else 128, bs,
                                      [3000, 1, 2049, 800], seed=91, extra_blocks=7,
                                      tail_k="nan", tail_v="nan"))
-    a = run(case)
-    b = run(kvgen.repermute(case, seed=92))
+    a = run(case, plan=device_plan(case, variant))
+    perm = kvgen.repermute(case, seed=92)
+    b = run(perm, plan=device_plan(perm, variant))
     assert np.array_equal(bits(a), bits(b))
 
 
-def test_run_to_run_deterministic():
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_run_to_run_deterministic(variant):
     case = configs.cfg4(24576, device="cuda")
-    a = bits(run(case))
+    plan = device_plan(case, variant)
+    a = bits(run(case, plan=plan))
     for _ in range(3):
-        assert np.array_equal(a, bits(run(case)))
+        assert np.array_equal(a, bits(run(case, plan=plan)))
 
 
 @pytest.mark.parametrize("mk", ["cfg2", "cfg4"])
@@ -226,15 +284,18 @@ TRACE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("rows", [0, 1])
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("D,bs,G,lens,forced", TRACE_CASES)
-def test_bookkeeping_trace_bit_exact(D, bs, G, lens, forced):
+def test_bookkeeping_trace_bit_exact(D, bs, G, lens, forced, variant, rows):
     Hkv = 2
     case = to_device(kvgen.make_case(len(lens), G * Hkv, Hkv, D, bs, lens, seed=101,
                                      extra_blocks=3))
     shape = shape_of(case)
     plan = pda.paged_decode_attn_plan(shape) if forced is None else plan_of(*forced)
+    plan.variant = VARIANTS[variant]
     slot, part, ranges = pda.paged_decode_attn_trace(shape, plan, case.block_table,
-                                                     case.seq_lens_t)
+                                                     case.seq_lens_t, rows=rows)
     torch.cuda.synchronize()
     e_slot, e_part, e_ranges, valid = bookkeeping.expected_trace(
         case.block_table.cpu().numpy(), case.seq_lens, Hkv, bs, case.max_seq_len,
@@ -247,12 +308,14 @@ def test_bookkeeping_trace_bit_exact(D, bs, G, lens, forced):
     assert np.array_equal(ranges, e_ranges)
 
 
-def test_bookkeeping_trace_cfg5_full_size():
+@pytest.mark.parametrize("variant,rows", [("valu", 0), ("mfma", 0), ("mfma", 1)])
+def test_bookkeeping_trace_cfg5_full_size(variant, rows):
     case = configs.cfg5(device="cuda")
     shape = shape_of(case)
     plan = pda.paged_decode_attn_plan(shape)
+    plan.variant = VARIANTS[variant]
     slot, part, ranges = pda.paged_decode_attn_trace(shape, plan, case.block_table,
-                                                     case.seq_lens_t)
+                                                     case.seq_lens_t, rows=rows)
     torch.cuda.synchronize()
     e_slot, e_part, e_ranges, valid = bookkeeping.expected_trace(
         case.block_table.cpu().numpy(), case.seq_lens, case.Hkv, case.bs, case.max_seq_len,
