@@ -72,27 +72,37 @@ extern "C" {
  *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
  * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs) and PV on
  *   v_mfma_f32_16x16x4_f32 (fp32 weights, exact fp32 V), the packed query
- *   group padded to 16 rows; G <= PDA_MAX_GROUP.
- * The plan picks VALU for G <= PDA_VALU_MAX_GROUP and MFMA above it. */
+ *   group padded to 16 rows; G <= PDA_MAX_GROUP. */
 #define PDA_VARIANT_VALU 1
 #define PDA_VARIANT_MFMA 2
 #define PDA_VALU_MAX_GROUP 8
 
-/* ---- the partition plan -------------------------------------------------
- * A pure integer function of (num_seqs B, num_kv_heads Hkv, head_size D,
- * max_seq_len Lmax, cu_count C).  With
- *   PDA_TILE          16   tokens per wavefront tile
- *   PDA_WAVES          4   wavefronts per workgroup
- *   PDA_TP_ALIGN      64   = PDA_TILE * PDA_WAVES, granularity of T_p
- *   PDA_WG_PER_CU      2   target number of workgroups per compute unit
- *   PDA_WG_MIN_BYTES  64 KiB and PDA_WG_MAX_BYTES 512 KiB of K+V per workgroup
- *   bpt   = 4 * D                            (K and V bytes per token, one KV head)
- *   T_min = max(ALIGN, floor(MIN_BYTES / bpt / ALIGN) * ALIGN)
- *   T_max = max(T_min, floor(MAX_BYTES / bpt / ALIGN) * ALIGN)
- *   units = B * Hkv
- *   P_tgt = ceil(WG_PER_CU * C / units)
- *   T_p   = clamp(roundup(ceil(Lmax / P_tgt), ALIGN), T_min, T_max)
- *   P     = max(1, ceil(Lmax / T_p))
+/* ---- the plan -------------------------------------------------------------
+ * A pure integer function of (num_seqs B, num_kv_heads Hkv, G = Hq/Hkv,
+ * head_size D, max_seq_len Lmax, compute-unit count C):
+ *
+ * Variant: MFMA if G > PDA_VALU_MAX_GROUP, or if G >= PDA_MFMA_MIN_GROUP and
+ *   B*Hkv <= PDA_MFMA_MAX_UNITS (few units: the lighter VALU load of the
+ *   matrix cores pays); VALU otherwise (many units: its higher occupancy
+ *   pays).
+ * R, workgroups resident per CU for that kernel (its register footprint):
+ *   1 for MFMA at D = 256, else 2.
+ * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D (K and V bytes per
+ *   token of one KV head):
+ *   T_min  = max(ALIGN, floor(PDA_WG_MIN_BYTES  / bpt / ALIGN) * ALIGN)
+ *   T_many = max(T_min, floor(PDA_WG_MANY_BYTES / bpt / ALIGN) * ALIGN)
+ *   T_one  = max(T_many, floor(PDA_WG_ONE_BYTES / bpt / ALIGN) * ALIGN)
+ *   P_fill = ceil(R * C / (B * Hkv))
+ *   T_fill = max(T_min, roundup(ceil(Lmax / P_fill), ALIGN))
+ *   T_p    = T_fill if T_fill <= T_one else T_many
+ *   P      = max(1, ceil(Lmax / T_p))
+ *   i.e. when one round of R*C workgroups covers the job at <= 1 MiB each,
+ *   use exactly that round (the split-KV partition count comes from the CU
+ *   occupancy); otherwise cut the job into 256 KiB workgroups and let the
+ *   hardware dispatcher balance them over many rounds.  (A second round of
+ *   the same size only exposes its start-up latency again, and a workgroup
+ *   that shares a CU with an older one is served later, so one round keeps
+ *   both halves of the CU busy to the end.)
  * Partition p of (b, g) covers tokens [p*T_p, min((p+1)*T_p, seq_lens[b]));
  * it is empty when p*T_p >= seq_lens[b].  The grid of the main kernel is
  * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
@@ -111,12 +121,13 @@ extern "C" {
  * every fused call leaves them zero again, so a workspace needs zeroing once
  * (paged_decode_attn_workspace_init, or any zero fill) before its first use.
  * Calls that run concurrently need separate workspaces. */
-#define PDA_TILE          16
-#define PDA_WAVES         4
-#define PDA_TP_ALIGN      64
-#define PDA_WG_PER_CU     2
-#define PDA_WG_MIN_BYTES  (64 * 1024)
-#define PDA_WG_MAX_BYTES  (512 * 1024)
+#define PDA_TILE            16
+#define PDA_TP_ALIGN        64
+#define PDA_MFMA_MIN_GROUP  4
+#define PDA_MFMA_MAX_UNITS  32
+#define PDA_WG_MIN_BYTES    (64 * 1024)
+#define PDA_WG_MANY_BYTES   (256 * 1024)
+#define PDA_WG_ONE_BYTES    (1024 * 1024)
 
 #define PDA_MERGE_FUSED   0
 #define PDA_MERGE_KERNEL  1

@@ -12,39 +12,57 @@ so the rule is this library's own; what the pages fix is the reason for it:
 (same page, the occupancy table and the paragraph under it).
 """
 
-TILE = 16
-WAVES = 4
-TP_ALIGN = TILE * WAVES
-WG_PER_CU = 2
+TP_ALIGN = 64
+VALU_MAX_GROUP = 8
+MFMA_MIN_GROUP = 4
+MFMA_MAX_UNITS = 32
 WG_MIN_BYTES = 64 * 1024
-WG_MAX_BYTES = 512 * 1024
+WG_MANY_BYTES = 256 * 1024
+WG_ONE_BYTES = 1024 * 1024
+VALU, MFMA = 1, 2
 
 
 def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
+def variant(num_seqs: int, num_kv_heads: int, group: int) -> int:
+    """MFMA above the VALU group limit, or for G >= 4 with few units."""
+    units = num_seqs * num_kv_heads
+    if group > VALU_MAX_GROUP or (group >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
+        return MFMA
+    return VALU
+
+
+def resident(var: int, head_size: int) -> int:
+    """Workgroups per CU the plan assumes for the chosen kernel."""
+    return 1 if (var == MFMA and head_size == 256) else 2
+
+
 def token_bounds(head_size: int):
-    """(T_min, T_max) in tokens for one workgroup."""
+    """(T_min, T_many, T_one) in tokens."""
     bpt = 4 * head_size  # K and V, 16-bit, one KV head
     t_min = max(TP_ALIGN, (WG_MIN_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
-    t_max = max(t_min, (WG_MAX_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
-    return t_min, t_max
+    t_many = max(t_min, (WG_MANY_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
+    t_one = max(t_many, (WG_ONE_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
+    return t_min, t_many, t_one
 
 
-def partition(num_seqs: int, num_kv_heads: int, head_size: int, max_seq_len: int,
+def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_seq_len: int,
               cu_count: int):
-    """(P, T_p) for the documented rule."""
-    t_min, t_max = token_bounds(head_size)
+    """(P, T_p, variant) for the documented rule."""
+    var = variant(num_seqs, num_kv_heads, group)
+    r = resident(var, head_size)
+    t_min, t_many, t_one = token_bounds(head_size)
     units = num_seqs * num_kv_heads
-    p_tgt = _cdiv(WG_PER_CU * cu_count, units)
+    p_fill = _cdiv(r * cu_count, units)
     if max_seq_len <= 0:
         t_p = t_min
     else:
-        t_p = _cdiv(_cdiv(max_seq_len, p_tgt), TP_ALIGN) * TP_ALIGN
-        t_p = min(max(t_p, t_min), t_max)
+        t_fill = max(t_min, _cdiv(_cdiv(max_seq_len, p_fill), TP_ALIGN) * TP_ALIGN)
+        t_p = t_fill if t_fill <= t_one else t_many
     p = max(1, _cdiv(max_seq_len, t_p))
-    return p, t_p
+    return p, t_p, var
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,

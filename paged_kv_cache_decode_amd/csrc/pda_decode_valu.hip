@@ -184,44 +184,38 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // partition's last tile re-reads that tile (a cache hit) to keep the loop
     // body free of branches around loads.
     const auto clampt = [&](int jj) { return min(jj, ntiles - 1); };
-    int j = wave;
-#if PDA_VALU_STAGES == 3
-    uint4 ka[U], va[U], kb[U], vb[U], kx[U], vx[U];
-    if (j < ntiles) {
-        load_tile(j, ka, va);
-        load_tile(clampt(j + kWaves), kb, vb);
-    }
-    for (; j < ntiles; j += 3 * kWaves) {
-        load_tile(clampt(j + 2 * kWaves), kx, vx);
-        PDA_SCHED_FENCE();
-        process(j, ka, va);
-        if (j + kWaves >= ntiles) break;
-        load_tile(clampt(j + 3 * kWaves), ka, va);
-        PDA_SCHED_FENCE();
-        process(j + kWaves, kb, vb);
-        if (j + 2 * kWaves >= ntiles) break;
-        load_tile(clampt(j + 4 * kWaves), kb, vb);
-        PDA_SCHED_FENCE();
-        process(j + 2 * kWaves, kx, vx);
-    }
-#else
-    // Loop rotated so that its head is a wait for buffer a while buffer b is
-    // already in flight.
-    uint4 ka[U], va[U], kb[U], vb[U];
-    if (j < ntiles) {
-        load_tile(j, ka, va);
-        load_tile(clampt(j + kWaves), kb, vb);
-    }
-    for (; j < ntiles; j += 2 * kWaves) {
-        process(j, ka, va);
-        if (j + kWaves >= ntiles) break;
-        load_tile(clampt(j + 2 * kWaves), ka, va);
-        PDA_SCHED_FENCE();
-        process(j + kWaves, kb, vb);
-        load_tile(clampt(j + 3 * kWaves), kb, vb);
-        PDA_SCHED_FENCE();
-    }
+    constexpr int S = PDA_VALU_STAGES;
+#if PDA_X_PRIO
+    const int prio_half = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 2 >=
+                          gridDim.x * gridDim.y * gridDim.z;
 #endif
+    static_assert(S >= 2 && S <= 8, "stages");
+    uint4 kbuf[S][U], vbuf[S][U];
+    int j = wave;
+    if (j < ntiles) {
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st) load_tile(clampt(j + st * kWaves), kbuf[st], vbuf[st]);
+    }
+    // Each step refills the buffer freed S-1 steps ago and then processes the
+    // oldest one, so S-1 tiles are in flight while one is processed.
+    for (; j < ntiles; j += S * kWaves) {
+        bool done = false;
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            if (!done) {
+                load_tile(clampt(j + (st + S - 1) * kWaves), kbuf[(st + S - 1) % S],
+                          vbuf[(st + S - 1) % S]);
+                PDA_SCHED_FENCE();
+#if PDA_X_PRIO
+                if (((j / kWaves + st) ^ prio_half) & 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+#endif
+                process(j + st * kWaves, kbuf[st], vbuf[st]);
+                done = j + (st + 1) * kWaves >= ntiles;
+            }
+        }
+        if (done) break;
+    }
 
     // merge the R lane sub-streams (lanes c, c+LPT, ...) of the wavefront
 #pragma unroll

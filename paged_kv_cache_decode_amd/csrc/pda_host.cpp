@@ -1,5 +1,6 @@
 // Host runtime of libpda.so: argument validation, the partition plan, the
 // workspace layout and the kernel launches behind the C ABI of pda.h.
+#include <algorithm>
 #include <atomic>
 #include <stdint.h>
 
@@ -175,28 +176,27 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     if (rc != PDA_OK) return rc;
     if (!plan || cu_count < 1) return PDA_ERR_INVALID;
     // the rule documented in pda.h
+    const int64_t G = s->num_q_heads / s->num_kv_heads;
+    const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
+    const bool mfma = G > PDA_VALU_MAX_GROUP ||
+                      (G >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
+    const int64_t resident = (mfma && s->head_size == 256) ? 1 : 2;
     const int64_t bpt = 4 * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
-    int64_t t_min = (PDA_WG_MIN_BYTES / bpt / align) * align;
-    if (t_min < align) t_min = align;
-    int64_t t_max = (PDA_WG_MAX_BYTES / bpt / align) * align;
-    if (t_max < t_min) t_max = t_min;
-    const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
-    const int64_t p_tgt = cdiv64((int64_t)PDA_WG_PER_CU * cu_count, units);
-    int64_t tp;
-    if (s->max_seq_len <= 0) {
-        tp = t_min;
-    } else {
-        tp = cdiv64(cdiv64(s->max_seq_len, p_tgt), align) * align;
-        if (tp < t_min) tp = t_min;
-        if (tp > t_max) tp = t_max;
+    const int64_t t_min = std::max(align, (PDA_WG_MIN_BYTES / bpt / align) * align);
+    const int64_t t_many = std::max(t_min, (PDA_WG_MANY_BYTES / bpt / align) * align);
+    const int64_t t_one = std::max(t_many, (PDA_WG_ONE_BYTES / bpt / align) * align);
+    const int64_t p_fill = cdiv64(resident * cu_count, units);
+    int64_t tp = t_min;
+    if (s->max_seq_len > 0) {
+        const int64_t t_fill = std::max(t_min, cdiv64(cdiv64(s->max_seq_len, p_fill), align) * align);
+        tp = t_fill <= t_one ? t_fill : t_many;
     }
     int64_t P = cdiv64(s->max_seq_len, tp);
     if (P < 1) P = 1;
     plan->num_partitions = (int32_t)P;
     plan->tokens_per_partition = (int32_t)tp;
-    plan->variant = s->num_q_heads / s->num_kv_heads > kValuMaxGroup ? PDA_VARIANT_MFMA
-                                                                      : PDA_VARIANT_VALU;
+    plan->variant = mfma ? PDA_VARIANT_MFMA : PDA_VARIANT_VALU;
     plan->merge = PDA_MERGE_KERNEL;
     plan->cu_count = cu_count;
     plan->workspace_bytes = pda_workspace_bytes(s, plan);

@@ -44,15 +44,15 @@ def test_plan_matches_oracle_plan(D):
     for _ in range(3000):
         B = int(rng.integers(1, 200))
         Hkv = int(rng.integers(1, 17))
-        G = int(rng.integers(1, 9))
+        G = int(rng.integers(1, 17))
         bs = int(rng.choice([1, 3, 16, 784]))
         L = int(rng.integers(0, 300000))
         mbs = max(1, -(-L // bs))
         cu = int(rng.choice([1, 7, 80, 256, 304]))
         shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16")
         got = pda.pda_plan_for_cus(shape, cu)
-        P, T = oplan.partition(B, Hkv, D, L, cu)
-        assert (got.num_partitions, got.tokens_per_partition) == (P, T)
+        P, T, var = oplan.partition(B, Hkv, G, D, L, cu)
+        assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
         assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv)
         assert got.merge == pda.PDA_MERGE_KERNEL
         assert got.cu_count == cu
@@ -63,10 +63,11 @@ def test_plan_golden_through_library():
     with open(os.path.join(ROOT, "tests", "golden", "plan_cu256.json")) as f:
         g = json.load(f)
     for c in g["cases"]:
-        shape = pda.make_shape(c["B"], c["Hkv"] * 2, c["Hkv"], c["D"], 16, 1,
+        shape = pda.make_shape(c["B"], c["Hkv"] * c["G"], c["Hkv"], c["D"], 16, 1,
                                max(1, -(-c["Lmax"] // 16)), c["Lmax"])
         got = pda.pda_plan_for_cus(shape, g["cu_count"])
-        assert (got.num_partitions, got.tokens_per_partition) == (c["P"], c["T_p"]), c["name"]
+        assert (got.num_partitions, got.tokens_per_partition, got.variant) == \
+            (c["P"], c["T_p"], c["variant"]), c["name"]
 
 
 BAD_SHAPES = [

@@ -17,26 +17,31 @@ def test_plan_hand_derived_values():
     with open(GOLDEN) as f:
         g = json.load(f)
     for c in g["cases"]:
-        P, T = plan.partition(c["B"], c["Hkv"], c["D"], c["Lmax"], g["cu_count"])
-        assert (P, T) == (c["P"], c["T_p"]), c["name"]
+        P, T, var = plan.partition(c["B"], c["Hkv"], c["G"], c["D"], c["Lmax"], g["cu_count"])
+        assert (P, T, var) == (c["P"], c["T_p"], c["variant"]), c["name"]
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_plan_invariants(D):
     rng = np.random.default_rng(D)
-    t_min, t_max = plan.token_bounds(D)
+    t_min, t_many, t_one = plan.token_bounds(D)
     for _ in range(2000):
         B = int(rng.integers(1, 129))
         Hkv = int(rng.integers(1, 33))
+        G = int(rng.integers(1, 17))
         L = int(rng.integers(0, 200000))
         cu = int(rng.choice([1, 80, 104, 256, 304]))
-        P, T = plan.partition(B, Hkv, D, L, cu)
-        assert T % plan.TP_ALIGN == 0 and t_min <= T <= t_max
+        P, T, var = plan.partition(B, Hkv, G, D, L, cu)
+        assert T % plan.TP_ALIGN == 0 and t_min <= T <= t_one
         assert P >= 1 and P * T >= L
         if L > 0:
             assert (P - 1) * T < L          # no partition is empty at Lmax
+            R = plan.resident(var, D)
+            # either one round fits the resident slots, or partitions are T_many
+            assert P * B * Hkv <= R * cu + B * Hkv or T == t_many
         else:
             assert P == 1
+        assert var == plan.MFMA if G > 8 else var in (plan.VALU, plan.MFMA)
 
 
 def test_workspace_bytes():
