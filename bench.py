@@ -35,6 +35,28 @@ PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 2 << 30     # >= 2 GiB of distinct KV between reuses of one pool
 
 
+def _cfg():
+    from kvgen import configs
+    return configs
+
+
+# The timed workload: the headline one by default; the others for profiling.
+WORKLOADS = {
+    "headline": dict(make=lambda: _cfg().cfg2(32, 32768, device="cuda"),
+                     desc="paged GQA decode, batch 1, 32 query / 8 KV heads, head 128, "
+                          "block 16, 32768-token context, bf16 KV ~N(0,1), permuted table"),
+    "cfg4-32K": dict(make=lambda: _cfg().cfg4(32768, device="cuda"),
+                     desc="low-parallelism decode, batch 1, 24 query / 4 KV heads, head 256, "
+                          "block 784, 32768-token context, bf16 KV ~N(0,1)"),
+    "cfg3-B8-32K": dict(make=lambda: _cfg().cfg3(8, 32768, device="cuda"),
+                        desc="gemma-like decode, batch 8, 32 query / 16 KV heads, head 128, "
+                             "block 16, 32768-token contexts, bf16 KV ~N(0,1)"),
+    "cfg5": dict(make=lambda: _cfg().cfg5(device="cuda"),
+                 desc="mixed-length decode, batch 64, 32 query / 8 KV heads, head 128, "
+                      "block 16, contexts U[1K, 32K], bf16 KV ~N(0,1), fragmented tables"),
+}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -51,7 +73,10 @@ def replicas_for(case):
 
 
 def time_case(case, steps, warmup, passes=1):
-    """Returns dict with per-call device time, split-KV kernel time, plan."""
+    """Per-call device time from passes of plain back-to-back calls (two HIP
+    events around the pass), and the split-KV kernel's own duration from
+    passes in which the library attaches events to that launch.  Returns a
+    dict with both, the plan and the last output."""
     import torch
     import paged_kv_cache_decode_amd as pda
     shape = pda.make_shape(case.B, case.Hq, case.Hkv, case.D, case.bs, case.num_blocks,
@@ -77,26 +102,32 @@ def time_case(case, steps, warmup, passes=1):
     for e in ev0 + ev1:
         e.record()  # materialise the HIP event before the library uses it
     torch.cuda.synchronize()
-    results = []
+    calls, kernels = [], []
     for _ in range(passes):
+        # plain pass: the whole decode step, nothing else on the stream
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         start.record()
         for i in range(steps):
-            call(i, ev0[i], ev1[i])
+            call(i)
         stop.record()
         torch.cuda.synchronize()
         w1 = time.perf_counter()
-        call_ms = start.elapsed_time(stop) / steps
-        kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / steps
-        results.append(dict(call_ms=call_ms, kernel_ms=kern_ms, wall_ms=(w1 - w0) * 1e3 / steps))
-    best = min(results, key=lambda r: r["call_ms"])
-    med = sorted(results, key=lambda r: r["call_ms"])[len(results) // 2]
+        calls.append(dict(call_ms=start.elapsed_time(stop) / steps,
+                          wall_ms=(w1 - w0) * 1e3 / steps))
+        # instrumented pass: events on the split-KV kernel's own launch
+        for i in range(steps):
+            call(i, ev0[i], ev1[i])
+        torch.cuda.synchronize()
+        kernels.append(sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / steps)
+    order = sorted(range(passes), key=lambda k: calls[k]["call_ms"])
+    med = order[len(order) // 2]
     kv = case.kv_bytes()
-    return dict(out=out, plan=plan, replicas=R, passes=results, call_ms=med["call_ms"],
-                kernel_ms=med["kernel_ms"], wall_ms=med["wall_ms"], best_call_ms=best["call_ms"],
+    return dict(out=out, plan=plan, replicas=R, passes=calls, call_ms=calls[med]["call_ms"],
+                wall_ms=calls[med]["wall_ms"], best_call_ms=calls[order[0]]["call_ms"],
+                kernel_ms=sorted(kernels)[len(kernels) // 2], kernel_passes=kernels,
                 kv_bytes=kv)
 
 
@@ -113,8 +144,35 @@ def summary(name, case, r):
             "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
             "kernel_GBps": round(kgbs, 1), "kernel_pct_of_peak": round(100 * kgbs / PEAK_GBS, 2),
             "us_per_context_token": round(us / sum(case.seq_lens), 6),
+            "variant": {1: "valu", 2: "mfma"}.get(r["plan"].variant, "?"),
             "replica_pools": r["replicas"],
             "passes_us": [round(p["call_ms"] * 1e3, 3) for p in r["passes"]]}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(variant: str):
+    """HBM bytes per launch of the headline split-KV kernel from the committed
+    rocprofv3 counter summary (profiles/traffic_headline.json), or None when
+    that summary was taken from other kernel sources than these."""
+    path = os.path.join(ROOT, "profiles", "traffic_headline.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("variant") != variant:
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(case, seconds):
@@ -148,6 +206,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS),
+                    help="the timed workload (default: the headline one)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -166,10 +226,11 @@ def main():
     log(f"library: {pda.pda_build_id()}")
 
     L = 32768
-    case = configs.cfg2(32, L, device="cuda")
-    log("timing headline workload (cfg2 Hq 32 / Hkv 8, 32K)")
+    wl = WORKLOADS[args.workload]
+    case = wl["make"]()
+    log(f"timing workload {args.workload}: {wl['desc']}")
     r = time_case(case, args.steps, args.warmup, passes=args.passes)
-    head = summary("paged_decode bf16 B1 Hq32 Hkv8 D128 bs16 L32768", case, r)
+    head = summary(args.workload, case, r)
 
     cpu = None
     parity = None
@@ -218,17 +279,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "paged GQA decode, batch 1, 32 query / 8 KV heads, head 128, "
-                               "block 16, 32768-token context, bf16 KV ~N(0,1), permuted table",
-                   "global_batch": 1, "seq_len": L, "parallelism": "single GPU"},
+        "config": {"workload": wl["desc"], "global_batch": case.B, "seq_len": case.max_seq_len,
+                   "parallelism": "single GPU"},
         "us_per_call": head["us_per_call"],
         "pct_of_peak": head["pct_of_peak"],
         "us_per_context_token": head["us_per_context_token"],
         "plan": {"P": head["P"], "T_p": head["T_p"], "replica_pools": head["replica_pools"]},
         "passes_us": head["passes_us"],
-        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel (split-KV)",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"decode_{head['variant']}_kernel (split-KV)",
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": measured_traffic(head["variant"]),
                      "kernel_us": round(r["kernel_ms"] * 1e3, 3),
                      "algorithmic_bytes_per_launch": kbytes},
         "cpu_baseline": cpu,
