@@ -61,7 +61,7 @@ struct MfmaQK<FP16> {
 
 // The element type and head size are template parameters of the kernel so
 // that every instantiation has its own symbol across translation units.
-template <typename Elt, int D, bool ALIGNED>
+template <typename Elt, int D, bool ALIGNED, bool BUF>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
@@ -85,7 +85,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int t1 = min(t0 + p.tokens_per_part, L);
     const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
     const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
-    stage_table_slice(p, b, lb0, lb1, tbl);
+    if (!ALIGNED) stage_table_slice(p, b, lb0, lb1, tbl);
+    const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
+    const int tlb0 = ALIGNED ? 0 : lb0;
 
     // Q^T as the B operand: head c16 of the group (zero rows past G),
     // elements 32s + 8*q4 .. +8 for k-step s
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             qb[s] = (c16 < G) ? *reinterpret_cast<const uint4*>(qrow + 32 * s)
                               : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+    if (!ALIGNED) __syncthreads();  // publish the staged table slice
 
     const char* kc = static_cast<const char*>(p.k_cache);
     const char* vc = static_cast<const char*>(p.v_cache);
@@ -107,24 +109,36 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const uint32_t v_lane = (uint32_t)(8 * (c16 % CW)) * 2;             // bytes
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
-    auto load_tile = [&](int j, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
-        const int tile_base = t0 + j * TT;
+    // Tile jj >= ntiles is a prefetch past the end: with buffer loads (BUF)
+    // it loads nothing (zeros, no memory access); otherwise it re-reads the
+    // last tile.  Either way process() never sees it.  Buffer loads need a
+    // wave-uniform block base (the aligned path); the launcher picks them
+    // where they measured faster (see launch_one).
+    static_assert(ALIGNED || !BUF, "buffer loads need the aligned path");
+    constexpr bool kBuf = BUF;
+    auto load_tile = [&](int jj, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
+        const bool valid = jj < ntiles;
+        const int tile_base = t0 + min(jj, ntiles - 1) * TT;
         int phys, slot0, dt;
-        locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, mfma_k_offset(lane), phys, slot0, dt);
+        locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, mfma_k_offset(lane), phys, slot0, dt);
         {
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + k_lane;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) kr[s] = load_row16(kc + base + off + 64 * s);
+            for (int s = 0; s < KS; ++s)
+                kr[s] = kBuf ? load_row16_buf(kc + base, off + 64 * s, valid)
+                             : load_row16(kc + base + off + 64 * s);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, mfma_v_offset(lane, r), phys, slot0,
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, mfma_v_offset(lane, r), phys, slot0,
                                 dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + v_lane;
 #pragma unroll
-            for (int dh = 0; dh < DH; ++dh) vr[r][dh] = load_row16(vc + base + off + 256 * dh);
+            for (int dh = 0; dh < DH; ++dh)
+                vr[r][dh] = kBuf ? load_row16_buf(vc + base, off + 256 * dh, valid)
+                                 : load_row16(vc + base + off + 256 * dh);
         }
     };
 
@@ -194,20 +208,22 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     };
 
     // Two register buffers, loop rotated so that its head waits for buffer a
-    // while buffer b is in flight (see the VALU variant).
-    const auto clampt = [&](int jj) { return min(jj, ntiles - 1); };
+    // while buffer b is in flight.  The loop has a single exit and its loads
+    // are unconditional (past the end they load nothing, see load_tile): an
+    // exit or a guarded load in the middle of the body makes the compiler
+    // drain every outstanding load (vmcnt(0)) at the loop head, which leaves
+    // one tile in flight instead of two.
     int j = wave;
     uint4 ka[KS], va[4][DH], kb[KS], vb[4][DH];
     if (j < ntiles) {
         load_tile(j, ka, va);
-        load_tile(clampt(j + kWaves), kb, vb);
+        load_tile(j + kWaves, kb, vb);
     }
     for (; j < ntiles; j += 2 * kWaves) {
         process(j, ka, va);
-        if (j + kWaves >= ntiles) break;
-        load_tile(clampt(j + 2 * kWaves), ka, va);
-        process(j + kWaves, kb, vb);
-        load_tile(clampt(j + 3 * kWaves), kb, vb);
+        load_tile(j + 2 * kWaves, ka, va);
+        if (j + kWaves < ntiles) process(j + kWaves, kb, vb);
+        load_tile(j + 3 * kWaves, kb, vb);
     }
 
     // full denominator of head c16 (all four lane groups hold the same m)
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
         __syncthreads();
         write_unit_rows<Elt, D>(p, red, kHeadChunk, h0, hn, b, g, part);
-        __syncthreads();
+        if (h0 + kHeadChunk < G) __syncthreads();  // before the next chunk reuses red
     }
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, L, b, g);
 }
@@ -248,17 +264,17 @@ using EltT = FP16;
 #endif
 constexpr int kHead = PDA_HEAD;
 
-template <bool ALIGNED>
+template <bool ALIGNED, bool BUF>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
     const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED>), grid, dim3(kThreads), lds,
-                              stream, start, stop, 0, p);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF>), grid, dim3(kThreads),
+                              lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED>), grid, dim3(kThreads), lds,
-                           stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF>), grid, dim3(kThreads),
+                           lds, stream, p);
     return hipGetLastError();
 }
 
@@ -267,8 +283,14 @@ static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t strea
 hipError_t PDA_CAT(launch_decode_mfma, PDA_DTYPE, PDA_HEAD)(bool aligned, const DecodeParams& p,
                                                             int batch, hipStream_t stream,
                                                             hipEvent_t e0, hipEvent_t e1) {
-    return aligned ? launch_one<true>(p, batch, stream, e0, e1)
-                   : launch_one<false>(p, batch, stream, e0, e1);
+    // Buffer loads (past-the-end prefetches cost nothing) measured faster at
+    // head sizes up to 128, and at 256 when a wave holds at most two tiles;
+    // for long partitions at 256 the compiler schedules the global-load form
+    // better (its next-tile loads issue earlier), ~7% faster.
+    const bool buf = kHead <= 128 || p.tokens_per_part <= 2 * kWaves * 16;
+    if (!aligned) return launch_one<false, false>(p, batch, stream, e0, e1);
+    return buf ? launch_one<true, true>(p, batch, stream, e0, e1)
+               : launch_one<true, false>(p, batch, stream, e0, e1);
 }
 
 }  // namespace pda

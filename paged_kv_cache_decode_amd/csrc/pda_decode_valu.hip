@@ -37,11 +37,6 @@
 #ifndef PDA_VALU_STAGES
 #define PDA_VALU_STAGES 3
 #endif
-#if PDA_VALU_SCHED_FENCE
-#define PDA_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define PDA_SCHED_FENCE() ((void)0)
-#endif
 
 namespace pda {
 
@@ -72,7 +67,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int t1 = min(t0 + p.tokens_per_part, L);
     const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
     const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
-    stage_table_slice(p, b, lb0, lb1, tbl);
+    if (!ALIGNED) stage_table_slice(p, b, lb0, lb1, tbl);
+    const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
+    const int tlb0 = ALIGNED ? 0 : lb0;
 
     // the packed query rows of this KV group: 8 elements per lane and head
     uint4 qv[GP];
@@ -84,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
             qv[i] = (i < G) ? *reinterpret_cast<const uint4*>(qb + (int64_t)i * D)
                             : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+    if (!ALIGNED) __syncthreads();  // publish the staged table slice
 
     const char* kc = static_cast<const char*>(p.k_cache);
     const char* vc = static_cast<const char*>(p.v_cache);
@@ -95,16 +92,29 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // Address of a round's row: a block base (wave-uniform on the aligned
     // path, so it stays in scalar registers) plus a 32-bit per-lane byte
     // offset, the form of a global load with a scalar base.
-    auto load_tile = [&](int j, uint4 (&kr)[U], uint4 (&vr)[U]) {
-        const int tile_base = t0 + j * TT;
+    // Tile jj >= ntiles is a prefetch past the end: with buffer loads it
+    // loads nothing (zeros, no memory access); otherwise it re-reads the last
+    // tile.  Either way process() never sees it.  Buffer loads need a
+    // wave-uniform block base (the aligned path); they are used where they
+    // measured faster, a group of one head (with more heads the compiler's
+    // schedule of the buffer form loses ~1%).
+    constexpr bool kBuf = ALIGNED && GP == 1;
+    auto load_tile = [&](int jj, uint4 (&kr)[U], uint4 (&vr)[U]) {
+        const bool valid = jj < ntiles;
+        const int tile_base = t0 + min(jj, ntiles - 1) * TT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int phys, slot0, dt;
-            locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
+            locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, t1, u, r, phys, slot0, dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + lane_off;
-            kr[u] = load_row16(kc + base + off);
-            vr[u] = load_row16(vc + base + off);
+            if constexpr (kBuf) {
+                kr[u] = load_row16_buf(kc + base, off, valid);
+                vr[u] = load_row16_buf(vc + base, off, valid);
+            } else {
+                kr[u] = load_row16(kc + base + off);
+                vr[u] = load_row16(vc + base + off);
+            }
         }
     };
 
@@ -180,41 +190,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 
     // Register buffers in rotation: while one tile is processed the wave's
     // next tile(s) are already in flight, and no buffer is ever copied (a copy
-    // would force a wait for the in-flight loads).  A load past the
-    // partition's last tile re-reads that tile (a cache hit) to keep the loop
-    // body free of branches around loads.
-    const auto clampt = [&](int jj) { return min(jj, ntiles - 1); };
+    // would force a wait for the in-flight loads).
     constexpr int S = PDA_VALU_STAGES;
-#if PDA_X_PRIO
-    const int prio_half = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 2 >=
-                          gridDim.x * gridDim.y * gridDim.z;
-#endif
     static_assert(S >= 2 && S <= 8, "stages");
     uint4 kbuf[S][U], vbuf[S][U];
     int j = wave;
     if (j < ntiles) {
 #pragma unroll
-        for (int st = 0; st < S - 1; ++st) load_tile(clampt(j + st * kWaves), kbuf[st], vbuf[st]);
+        for (int st = 0; st < S - 1; ++st) load_tile(j + st * kWaves, kbuf[st], vbuf[st]);
     }
     // Each step refills the buffer freed S-1 steps ago and then processes the
-    // oldest one, so S-1 tiles are in flight while one is processed.
+    // oldest one, so S-1 tiles are in flight while one is processed.  One
+    // exit, unconditional loads (past the end they load nothing): see the
+    // note at load_row16_buf.
     for (; j < ntiles; j += S * kWaves) {
-        bool done = false;
 #pragma unroll
         for (int st = 0; st < S; ++st) {
-            if (!done) {
-                load_tile(clampt(j + (st + S - 1) * kWaves), kbuf[(st + S - 1) % S],
-                          vbuf[(st + S - 1) % S]);
-                PDA_SCHED_FENCE();
-#if PDA_X_PRIO
-                if (((j / kWaves + st) ^ prio_half) & 1) __builtin_amdgcn_s_setprio(1);
-                else __builtin_amdgcn_s_setprio(0);
-#endif
-                process(j + st * kWaves, kbuf[st], vbuf[st]);
-                done = j + (st + 1) * kWaves >= ntiles;
-            }
+            load_tile(j + (st + S - 1) * kWaves, kbuf[(st + S - 1) % S], vbuf[(st + S - 1) % S]);
+            if (j + st * kWaves < ntiles) process(j + st * kWaves, kbuf[st], vbuf[st]);
         }
-        if (done) break;
     }
 
     // merge the R lane sub-streams (lanes c, c+LPT, ...) of the wavefront

@@ -64,6 +64,26 @@ __device__ inline uint4 load_row16(const char* ptr) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The same 16 bytes at base + off through a buffer resource.  `base` must be
+// wave-uniform (it rides in scalar registers); `off` is the lane's byte
+// offset.  With `valid` false the resource holds no records, so the load
+// returns zeros without touching memory: the software pipelines use it to
+// prefetch "tiles" past the end with no traffic and no extra latency, keeping
+// every load in the loop unconditional (a guarded load or an early exit makes
+// the compiler drain all outstanding loads at the loop head).
+// Word 3 of the resource: 32-bit data format, as raw buffer loads need.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ inline uint4 load_row16_buf(const char* base, uint32_t off, bool valid) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base), (short)0, valid ? 0x7fffffff : 0, kBufferWord3);
+#if PDA_VALU_NT
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 2);  // nt
+#else
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+#endif
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Device-scope (all XCDs) store and load of fp32 workspace data: the store
 // is written through to the device coherence point (sc1), the load reads
 // from it, so partials written by one workgroup can be read by another on a
@@ -138,6 +158,14 @@ struct ValuGeom {
 // ---- block-table bookkeeping --------------------------------------------
 // The partition's slice of the sequence's block-table row is staged in LDS:
 // entries for logical blocks lb0 .. lb1 of tokens [t0, t1).
+// The block-table view locate_row takes: for ALIGNED kernels the global row
+// of sequence b (scalar loads, lb0 = 0); otherwise the LDS slice, which the
+// caller stages with stage_table_slice and publishes with a barrier.
+template <bool ALIGNED>
+__device__ inline const int32_t* table_view(const DecodeParams& p, int b, const int32_t* lds) {
+    return ALIGNED ? p.block_table + (int64_t)b * p.max_blocks_per_seq : lds;
+}
+
 __device__ inline void stage_table_slice(const DecodeParams& p, int b, int lb0, int lb1,
                                          int32_t* tbl) {
     const int32_t* row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
@@ -161,9 +189,11 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
 //  tokens or of the round length): all offsets a wave reads together lie in
 //  the 16-token group that contains offset o0 (wave-uniform), which lies in
 //  one block; phys and slot0 are located once from o0 and are wave-uniform,
-//  dt is the lane's row offset.
-//  Otherwise every lane divides its own token index by the block size and
-//  dt = 0.
+//  dt is the lane's row offset.  `tbl` is then the sequence's block-table row
+//  in global memory (lb0 = 0), read with a scalar load at the wave-uniform
+//  index: no staging, no barrier, and no vector register is taken.
+//  Otherwise `tbl` is the LDS copy of the slice starting at block lb0, every
+//  lane divides its own token index by the block size and dt = 0.
 template <bool ALIGNED>
 __device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int lb0,
                                   int tile_base, int t1, int o0, int o, int& phys, int& slot0,
@@ -175,7 +205,8 @@ __device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int
         const int lb = (int)fastdiv((uint32_t)ub, p.bs_div);
         slot0 = ub - lb * p.block_size;
         dt = t - ub;
-        phys = __builtin_amdgcn_readfirstlane(tbl[lb - lb0]);
+        typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+        phys = ((const_i32p)tbl)[lb - lb0];  // address-space cast: C-style only
         phys = min(max(phys, 0), p.num_blocks - 1);
     } else {
         const int lb = (int)fastdiv((uint32_t)t, p.bs_div);

@@ -6,13 +6,14 @@
 // p of query head h left a normalised fp32 output o_p, its max score m_p (exp2
 // domain) and its denominator l_p.  The exact softmax over the union is
 //     M = max_p m_p,   w_p = l_p * 2^(m_p - M),   out = sum_p w_p o_p / sum_p w_p
-// over the partitions that hold tokens (p < ceil(L / T_p)); empty partitions
-// are never read.  L == 0 gives a zero row.
+// over the partitions that hold tokens (p < ceil(L / T_p)); the stale
+// workspace entries of empty partitions may be loaded but never enter the
+// sums.  L == 0 gives a zero row.
 //
 // One workgroup of 256 threads per (64-element chunk of D, query head,
 // sequence): 16 lanes x 4 elements cover the chunk, 16 partition groups
-// stride over p.  Each thread merges its partitions with a running max after
-// one batch of loads; the 16 groups are then combined in a fixed order
+// stride over p.  Each thread merges its partitions with a running max, a
+// batch of loads at a time; the 16 groups are then combined in a fixed order
 // through LDS, so the result does not depend on timing.
 #include "pda_device.h"
 
@@ -25,31 +26,35 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     __shared__ float2 red_mw[16][16];
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, d4 = tid & 15, pg = tid >> 4;
-    const int L = context_len(p, b);
-    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
     const int64_t row = (int64_t)b * p.num_q_heads + h;
     uint16_t* out = static_cast<uint16_t*>(p.out) + row * D + chunk * 64 + d4 * 4;
+    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.num_partitions;
+    const float* po = p.ws_o + row * p.num_partitions * D + chunk * 64 + d4 * 4;
 
+    // The first batch of this thread's partitions (pg, pg+16, ...) is loaded
+    // before the context length is known: every index is inside the
+    // workspace, so the loads can leave together with the seq_lens load and
+    // the kernel pays one memory round trip instead of two.  Entries of
+    // partitions past the live ones hold stale data and are never used.
+    float2 mlv[kBatch];
+    float4 ov[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+        const int q = min(pg + 16 * k, p.num_partitions - 1);
+        mlv[k] = ml[q];
+        ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+    }
+    const int L = context_len(p, b);
+    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
     if (Pb == 0) {
         if (pg == 0) { out[0] = 0; out[1] = 0; out[2] = 0; out[3] = 0; }
         return;
     }
-    const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.num_partitions;
-    const float* po = p.ws_o + row * p.num_partitions * D + chunk * 64 + d4 * 4;
 
-    // This thread's partitions pg, pg+16, ...: all loads of a batch are issued
-    // before any is used, then combined with a running max (exp2 domain).
+    // Combine with a running max (exp2 domain), batch by batch.
     float M = -FLT_MAX, W = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q0 = pg; q0 < Pb; q0 += 16 * kBatch) {
-        float2 mlv[kBatch];
-        float4 ov[kBatch];
-#pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int q = min(q0 + 16 * k, Pb - 1);
-            mlv[k] = ml[q];
-            ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
-        }
+    for (int q0 = pg;;) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             if (q0 + 16 * k >= Pb) break;
@@ -60,6 +65,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
             O.z = O.z * sc + w * ov[k].z; O.w = O.w * sc + w * ov[k].w;
             W = W * sc + w;
             M = mn;
+        }
+        q0 += 16 * kBatch;
+        if (q0 >= Pb) break;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int q = min(q0 + 16 * k, Pb - 1);
+            mlv[k] = ml[q];
+            ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
         }
     }
     red_o[pg][d4] = O;

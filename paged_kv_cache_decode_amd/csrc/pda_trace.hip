@@ -33,8 +33,12 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     if (t0 >= L) return;
     const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
     const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
-    stage_table_slice(p, b, lb0, lb1, tbl);
-    __syncthreads();
+    if (!ALIGNED) {
+        stage_table_slice(p, b, lb0, lb1, tbl);
+        __syncthreads();
+    }
+    const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
+    const int tlb0 = ALIGNED ? 0 : lb0;
     const int ntiles = (t1 - t0 + TT - 1) / TT;
     auto record = [&](int t, int phys, int slot) {
         const int64_t at = unit * p.max_seq_len + t;
@@ -47,19 +51,19 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
         if constexpr (ROWS == 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                locate_token<R, ALIGNED>(p, tbl, lb0, tile_base, t1, u, r, phys, slot0, dt);
+                locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, t1, u, r, phys, slot0, dt);
                 const int t = tile_base + u * R + r;
                 if (c == 0 && t < t1) record(t, phys, slot0 + dt);
             }
         } else if constexpr (ROWS == 1) {
             const int o = mfma_k_offset(lane);
-            locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, o, phys, slot0, dt);
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, o, phys, slot0, dt);
             if ((lane >> 4) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int o = mfma_v_offset(lane, rr);
-                locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, 0, o, phys, slot0, dt);
+                locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, o, phys, slot0, dt);
                 if ((lane & 15) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
             }
         }
