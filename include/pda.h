@@ -85,24 +85,22 @@ extern "C" {
  *   B*Hkv <= PDA_MFMA_MAX_UNITS (few units: the lighter VALU load of the
  *   matrix cores pays); VALU otherwise (many units: its higher occupancy
  *   pays).
- * R, workgroups resident per CU for that kernel (its register footprint):
- *   1 for MFMA at D = 256, else 2.
  * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D (K and V bytes per
  *   token of one KV head):
  *   T_min  = max(ALIGN, floor(PDA_WG_MIN_BYTES  / bpt / ALIGN) * ALIGN)
  *   T_many = max(T_min, floor(PDA_WG_MANY_BYTES / bpt / ALIGN) * ALIGN)
  *   T_one  = max(T_many, floor(PDA_WG_ONE_BYTES / bpt / ALIGN) * ALIGN)
- *   P_fill = ceil(R * C / (B * Hkv))
+ *   P_fill = ceil(C / (B * Hkv))
  *   T_fill = max(T_min, roundup(ceil(Lmax / P_fill), ALIGN))
  *   T_p    = T_fill if T_fill <= T_one else T_many
  *   P      = max(1, ceil(Lmax / T_p))
- *   i.e. when one round of R*C workgroups covers the job at <= 1 MiB each,
- *   use exactly that round (the split-KV partition count comes from the CU
- *   occupancy); otherwise cut the job into 256 KiB workgroups and let the
- *   hardware dispatcher balance them over many rounds.  (A second round of
- *   the same size only exposes its start-up latency again, and a workgroup
- *   that shares a CU with an older one is served later, so one round keeps
- *   both halves of the CU busy to the end.)
+ *   i.e. when one round of C workgroups, one per compute unit, covers the
+ *   job at <= 1 MiB each, use exactly that round (the split-KV partition
+ *   count comes from the CU count); otherwise cut the job into 256 KiB
+ *   workgroups and let the hardware dispatcher balance them over many
+ *   rounds.  (Every extra round, and every second workgroup on a CU, exposes
+ *   a workgroup's start-up and epilogue again and doubles the partials the
+ *   merge reads; one workgroup per CU measured fastest for both variants.)
  * Partition p of (b, g) covers tokens [p*T_p, min((p+1)*T_p, seq_lens[b]));
  * it is empty when p*T_p >= seq_lens[b].  The grid of the main kernel is
  * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no

@@ -34,11 +34,6 @@ def variant(num_seqs: int, num_kv_heads: int, group: int) -> int:
     return VALU
 
 
-def resident(var: int, head_size: int) -> int:
-    """Workgroups per CU the plan assumes for the chosen kernel."""
-    return 1 if (var == MFMA and head_size == 256) else 2
-
-
 def token_bounds(head_size: int):
     """(T_min, T_many, T_one) in tokens."""
     bpt = 4 * head_size  # K and V, 16-bit, one KV head
@@ -52,10 +47,9 @@ def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_
               cu_count: int):
     """(P, T_p, variant) for the documented rule."""
     var = variant(num_seqs, num_kv_heads, group)
-    r = resident(var, head_size)
     t_min, t_many, t_one = token_bounds(head_size)
     units = num_seqs * num_kv_heads
-    p_fill = _cdiv(r * cu_count, units)
+    p_fill = _cdiv(cu_count, units)
     if max_seq_len <= 0:
         t_p = t_min
     else:

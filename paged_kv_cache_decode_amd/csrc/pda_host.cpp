@@ -180,13 +180,12 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
     const bool mfma = G > PDA_VALU_MAX_GROUP ||
                       (G >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
-    const int64_t resident = (mfma && s->head_size == 256) ? 1 : 2;
     const int64_t bpt = 4 * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
     const int64_t t_min = std::max(align, (PDA_WG_MIN_BYTES / bpt / align) * align);
     const int64_t t_many = std::max(t_min, (PDA_WG_MANY_BYTES / bpt / align) * align);
     const int64_t t_one = std::max(t_many, (PDA_WG_ONE_BYTES / bpt / align) * align);
-    const int64_t p_fill = cdiv64(resident * cu_count, units);
+    const int64_t p_fill = cdiv64(cu_count, units);
     int64_t tp = t_min;
     if (s->max_seq_len > 0) {
         const int64_t t_fill = std::max(t_min, cdiv64(cdiv64(s->max_seq_len, p_fill), align) * align);

@@ -36,9 +36,9 @@ def test_plan_invariants(D):
         assert P >= 1 and P * T >= L
         if L > 0:
             assert (P - 1) * T < L          # no partition is empty at Lmax
-            R = plan.resident(var, D)
-            # either one round fits the resident slots, or partitions are T_many
-            assert P * B * Hkv <= R * cu + B * Hkv or T == t_many
+            # either one round of one workgroup per CU covers the job, or the
+            # partitions are T_many
+            assert P * B * Hkv <= cu + B * Hkv or T == t_many
         else:
             assert P == 1
         assert var == plan.MFMA if G > 8 else var in (plan.VALU, plan.MFMA)
