@@ -149,14 +149,19 @@ def summary(name, case, r):
             "passes_us": [round(p["call_ms"] * 1e3, 3) for p in r["passes"]]}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and headers the library is built from."""
+def kernel_source_hash(variant: str = "mfma") -> str:
+    """sha256 over the sources the split-KV kernel of `variant` is compiled
+    from (its translation unit, the device and common headers, the C ABI
+    header): a change to any of them makes a committed counter summary of
+    that kernel stale; changes to other kernels (the merge) do not."""
     import hashlib
     h = hashlib.sha256()
-    for d in (os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc"), os.path.join(ROOT, "include")):
-        for f in sorted(os.listdir(d)):
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+    csrc = os.path.join(ROOT, "paged_kv_cache_decode_amd", "csrc")
+    files = [os.path.join(csrc, f"pda_decode_{variant}.hip"), os.path.join(csrc, "pda_device.h"),
+             os.path.join(csrc, "pda_common.h"), os.path.join(ROOT, "include", "pda.h")]
+    for path in files:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -170,7 +175,7 @@ def measured_traffic(variant: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("variant") != variant:
+    if t.get("variant") != variant or t.get("kernel_source_sha256") != kernel_source_hash(variant):
         return None
     return t.get("hbm_bytes_per_launch")
 

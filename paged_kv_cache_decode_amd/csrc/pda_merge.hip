@@ -19,7 +19,7 @@
 
 namespace pda {
 
-template <typename Elt, int D>
+template <typename Elt, int D, bool AHEAD>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     constexpr int kBatch = 8;  // partitions per thread and memory round trip
     __shared__ float4 red_o[16][16];
@@ -31,21 +31,36 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.num_partitions;
     const float* po = p.ws_o + row * p.num_partitions * D + chunk * 64 + d4 * 4;
 
-    // The first batch of this thread's partitions (pg, pg+16, ...) is loaded
-    // before the context length is known: every index is inside the
-    // workspace, so the loads can leave together with the seq_lens load and
-    // the kernel pays one memory round trip instead of two.  Entries of
-    // partitions past the live ones hold stale data and are never used.
+    // AHEAD (few rows, latency-bound): the first batch of this thread's
+    // partitions (pg, pg+16, ... below P) is loaded before the context length
+    // is known, so the loads leave together with the seq_lens load and the
+    // kernel pays one memory round trip instead of two; entries of partitions
+    // past the live ones hold stale data and are never used.  Otherwise (many
+    // rows, bandwidth-bound) only the live partitions are loaded.
     float2 mlv[kBatch];
     float4 ov[kBatch];
+    if constexpr (AHEAD) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-        const int q = min(pg + 16 * k, p.num_partitions - 1);
-        mlv[k] = ml[q];
-        ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+        for (int k = 0; k < kBatch; ++k) {
+            const int q = pg + 16 * k;
+            if (q < p.num_partitions) {
+                mlv[k] = ml[q];
+                ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+            }
+        }
     }
     const int L = context_len(p, b);
     const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
+    if constexpr (!AHEAD) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int q = pg + 16 * k;
+            if (q < Pb) {
+                mlv[k] = ml[q];
+                ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+            }
+        }
+    }
     if (Pb == 0) {
         if (pg == 0) { out[0] = 0; out[1] = 0; out[2] = 0; out[3] = 0; }
         return;
@@ -70,9 +85,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
         if (q0 >= Pb) break;
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const int q = min(q0 + 16 * k, Pb - 1);
-            mlv[k] = ml[q];
-            ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+            const int q = q0 + 16 * k;
+            if (q < Pb) {
+                mlv[k] = ml[q];
+                ov[k] = *reinterpret_cast<const float4*>(po + (int64_t)q * D);
+            }
         }
     }
     red_o[pg][d4] = O;
@@ -103,7 +120,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 template <typename Elt, int D>
 static hipError_t launch_merge_t(const DecodeParams& p, int batch, hipStream_t stream) {
     const dim3 grid(D / 64, p.num_q_heads, batch);
-    hipLaunchKernelGGL((merge_kernel<Elt, D>), grid, dim3(256), 0, stream, p);
+    // loading ahead of seq_lens pays when the merge is latency-bound (few
+    // rows); with many rows it would read every partition slot, live or not
+    if ((int64_t)batch * p.num_q_heads <= 256)
+        hipLaunchKernelGGL((merge_kernel<Elt, D, true>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((merge_kernel<Elt, D, false>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
