@@ -61,7 +61,34 @@ struct MfmaQK<FP16> {
 
 // The element type and head size are template parameters of the kernel so
 // that every instantiation has its own symbol across translation units.
-template <typename Elt, int D, bool ALIGNED, bool BUF>
+// 16-lane-row operand exchange for the 4-head-block PV: lane l takes the
+// value of lane (l & 0b110011) | (grp << 2), i.e. the lane of its own token
+// group (bits 4-5) that holds head 4*grp + (l & 3) (bits 2-3 select the head
+// group).  ds_swizzle in bit-mask mode: and 0x13, or grp << 2, within 32 lanes.
+template <int GRP>
+__device__ inline float take_head_of_group(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x13 | (GRP << 7)));
+}
+
+// Sum of a lane value over the four token groups (lanes l, l^16, l^32,
+// l^48), in the fixed order (g0 + g1) + (g2 + g3), with the gfx950 row and
+// half swaps (VALU, no LDS).
+__device__ inline float sum_token_groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
+                                                    false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// NG = 0: PV on v_mfma_f32_16x16x4_f32 with the group padded to 16 heads.
+// NG = 1, 2: PV on v_mfma_f32_4x4x1_16b_f32, NG groups of 4 heads: block
+// (lanes 4k..4k+3) = one token (the lane's V row of the round) x 4 columns
+// of d, rows = the 4 heads of a group; no padding to 16, a quarter of the
+// matrix-core cycles per head group.  Each lane group (l / 16) accumulates
+// over its own tokens; the four partial sums are added once at the end.
+template <typename Elt, int D, bool ALIGNED, bool BUF, int NG>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
@@ -142,11 +169,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
     };
 
-    f32x4_t oacc[DH][8];
+    // NG = 0: oacc[0][dh][e][r] = O[head 4*q4 + r][d = dh*128 + 8*c16 + e]
+    // NG > 0: oacc[grp][dh][e][i] = O[head 4*grp + i][same d], partial over
+    //         the tokens of lane group q4
+    constexpr int NA = NG == 0 ? 1 : NG;
+    f32x4_t oacc[NA][DH][8];
 #pragma unroll
-    for (int dh = 0; dh < DH; ++dh)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[a][dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -FLT_MAX;  // running max of head c16 (finite floor: exp2(-inf - m) = 0)
     float l = 0.f;       // this lane's share of head c16's denominator
 
@@ -171,16 +204,34 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         if (__builtin_amdgcn_ballot_w64(mn > m)) {
             const float alpha = fast_exp2(m - mn);
             l *= alpha;
-            // the accumulator rows of this lane are heads 4*q4 + r
-            float ar[4];
+            if constexpr (NG == 0) {
+                // the accumulator rows of this lane are heads 4*q4 + r
+                float ar[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+                for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
 #pragma unroll
-            for (int dh = 0; dh < DH; ++dh)
+                for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+                    for (int e = 0; e < 8; ++e)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) oacc[dh][e][r] *= ar[r];
+                        for (int r = 0; r < 4; ++r) oacc[0][dh][e][r] *= ar[r];
+            } else {
+                // heads 4*grp + i: their factors sit in lanes 4*grp + i
+#pragma unroll
+                for (int grp = 0; grp < NG; ++grp) {
+                    float ar[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ar[i] = __int_as_float(
+                            __builtin_amdgcn_readlane(__float_as_int(alpha), 4 * grp + i));
+#pragma unroll
+                    for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) oacc[grp][dh][e][i] *= ar[i];
+                }
+            }
             m = mn;
         }
         float pr[4];
@@ -188,6 +239,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r) {
             pr[r] = fast_exp2(sc[r] - m);
             l += pr[r];
+        }
+        // A operand of the 4-head blocks: lane 4k + i needs head 4*grp + i
+        float pa[NA][4];
+        if constexpr (NG > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pa[0][r] = take_head_of_group<0>(pr[r]);
+                if constexpr (NG > 1) pa[1][r] = take_head_of_group<1>(pr[r]);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -199,10 +259,19 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 vf[2] = Elt::lo(w.y); vf[3] = Elt::hi(w.y);
                 vf[4] = Elt::lo(w.z); vf[5] = Elt::hi(w.z);
                 vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
+                if constexpr (NG == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    oacc[dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pr[r], vf[e], oacc[dh][e],
-                                                                      0, 0, 0);
+                    for (int e = 0; e < 8; ++e)
+                        oacc[0][dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            pr[r], vf[e], oacc[0][dh][e], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            oacc[grp][dh][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(
+                                pa[grp][r], vf[e], oacc[grp][dh][e], 0, 0, 0);
+                }
             }
         }
     };
@@ -229,20 +298,50 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // full denominator of head c16 (all four lane groups hold the same m)
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if constexpr (NG > 0) {  // add the four lane groups' partial sums
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+            for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        oacc[grp][dh][e][i] = sum_token_groups(oacc[grp][dh][e][i]);
+    }
 
     // merge the wavefronts and write the unit's result, heads in chunks
     for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
         const int hn = min(kHeadChunk, G - h0);
-        if (c16 < CW) {
+        if constexpr (NG == 0) {
+            if (c16 < CW) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int hi = 4 * q4 + r - h0;
-                if (hi < 0 || hi >= hn) continue;
-                float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+                for (int r = 0; r < 4; ++r) {
+                    const int hi = 4 * q4 + r - h0;
+                    if (hi < 0 || hi >= hn) continue;
+                    float* row = red + (wave * kHeadChunk + hi) * (D + 2);
 #pragma unroll
-                for (int dh = 0; dh < DH; ++dh)
+                    for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) row[dh * 128 + 8 * c16 + e] = oacc[dh][e][r];
+                        for (int e = 0; e < 8; ++e)
+                            row[dh * 128 + 8 * c16 + e] = oacc[0][dh][e][r];
+                }
+            }
+        } else {
+            if (q4 == 0 && c16 < CW) {
+#pragma unroll
+                for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int hi = 4 * grp + i - h0;
+                        if (hi < 0 || hi >= hn) continue;
+                        float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+#pragma unroll
+                        for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                row[dh * 128 + 8 * c16 + e] = oacc[grp][dh][e][i];
+                    }
             }
         }
         if (q4 == 0 && c16 >= h0 && c16 < h0 + hn) {
@@ -264,18 +363,32 @@ using EltT = FP16;
 #endif
 constexpr int kHead = PDA_HEAD;
 
-template <bool ALIGNED, bool BUF>
+template <bool ALIGNED, bool BUF, int NG>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
     const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF>), grid, dim3(kThreads),
-                              lds, stream, start, stop, 0, p);
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG>), grid,
+                              dim3(kThreads), lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF>), grid, dim3(kThreads),
-                           lds, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG>), grid,
+                           dim3(kThreads), lds, stream, p);
     return hipGetLastError();
+}
+
+// PV form by group size: 4-head blocks for up to 4 heads, and for up to 8
+// at head sizes up to 128, where they take at most half the matrix-core
+// cycles of the padded 16-head form; the padded form otherwise (two 4-head
+// groups at head size 256 need more registers than a wave has: their
+// accumulators hold four token-group partials per output).
+template <bool ALIGNED, bool BUF>
+static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
+    if (p.group <= 4) return launch_one<ALIGNED, BUF, 1>(p, batch, stream, start, stop);
+    if constexpr (kHead <= 128)
+        if (p.group <= 8) return launch_one<ALIGNED, BUF, 2>(p, batch, stream, start, stop);
+    return launch_one<ALIGNED, BUF, 0>(p, batch, stream, start, stop);
 }
 
 #define PDA_CAT2(a, b, c) a##_##b##_##c
@@ -288,9 +401,9 @@ hipError_t PDA_CAT(launch_decode_mfma, PDA_DTYPE, PDA_HEAD)(bool aligned, const 
     // for long partitions at 256 the compiler schedules the global-load form
     // better (its next-tile loads issue earlier), ~7% faster.
     const bool buf = kHead <= 128 || p.tokens_per_part <= 2 * kWaves * 16;
-    if (!aligned) return launch_one<false, false>(p, batch, stream, e0, e1);
-    return buf ? launch_one<true, true>(p, batch, stream, e0, e1)
-               : launch_one<true, false>(p, batch, stream, e0, e1);
+    if (!aligned) return launch_pv<false, false>(p, batch, stream, e0, e1);
+    return buf ? launch_pv<true, true>(p, batch, stream, e0, e1)
+               : launch_pv<true, false>(p, batch, stream, e0, e1);
 }
 
 }  // namespace pda
