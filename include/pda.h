@@ -70,9 +70,11 @@ extern "C" {
 /* ---- kernel variants --------------------------------------------------- */
 /* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
  *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
- * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs) and PV on
- *   v_mfma_f32_16x16x4_f32 (fp32 weights, exact fp32 V), the packed query
- *   group padded to 16 rows; G <= PDA_MAX_GROUP. */
+ * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs, the
+ *   packed query group padded to 16 rows) and PV with fp32 weights and exact
+ *   fp32 V, on v_mfma_f32_4x4x1_16b_f32 blocks of 4 heads for G <= 4 (and
+ *   G <= 8 at head sizes up to 128), else on v_mfma_f32_16x16x4_f32 with the
+ *   group padded to 16; G <= PDA_MAX_GROUP. */
 #define PDA_VARIANT_VALU 1
 #define PDA_VARIANT_MFMA 2
 #define PDA_VALU_MAX_GROUP 8
@@ -82,9 +84,10 @@ extern "C" {
  * head_size D, max_seq_len Lmax, compute-unit count C):
  *
  * Variant: MFMA if G > PDA_VALU_MAX_GROUP, or if G >= PDA_MFMA_MIN_GROUP and
- *   B*Hkv <= PDA_MFMA_MAX_UNITS (few units: the lighter VALU load of the
- *   matrix cores pays); VALU otherwise (many units: its higher occupancy
- *   pays).
+ *   B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU load of the matrix cores
+ *   pays); VALU otherwise (one head per group, where the VALU kernel has
+ *   the least to do, or many units over many rounds, where its higher
+ *   occupancy pays).
  * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D (K and V bytes per
  *   token of one KV head):
  *   T_min  = max(ALIGN, floor(PDA_WG_MIN_BYTES  / bpt / ALIGN) * ALIGN)
@@ -121,8 +124,8 @@ extern "C" {
  * Calls that run concurrently need separate workspaces. */
 #define PDA_TILE            16
 #define PDA_TP_ALIGN        64
-#define PDA_MFMA_MIN_GROUP  4
-#define PDA_MFMA_MAX_UNITS  32
+#define PDA_MFMA_MIN_GROUP  2
+#define PDA_MFMA_MAX_UNITS  128
 #define PDA_WG_MIN_BYTES    (64 * 1024)
 #define PDA_WG_MANY_BYTES   (256 * 1024)
 #define PDA_WG_ONE_BYTES    (1024 * 1024)

@@ -14,8 +14,8 @@ so the rule is this library's own; what the pages fix is the reason for it:
 
 TP_ALIGN = 64
 VALU_MAX_GROUP = 8
-MFMA_MIN_GROUP = 4
-MFMA_MAX_UNITS = 32
+MFMA_MIN_GROUP = 2
+MFMA_MAX_UNITS = 128
 WG_MIN_BYTES = 64 * 1024
 WG_MANY_BYTES = 256 * 1024
 WG_ONE_BYTES = 1024 * 1024
@@ -27,7 +27,7 @@ def _cdiv(a: int, b: int) -> int:
 
 
 def variant(num_seqs: int, num_kv_heads: int, group: int) -> int:
-    """MFMA above the VALU group limit, or for G >= 4 with few units."""
+    """MFMA above the VALU group limit, or for G >= 2 with at most 128 units."""
     units = num_seqs * num_kv_heads
     if group > VALU_MAX_GROUP or (group >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
         return MFMA
