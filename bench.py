@@ -94,7 +94,9 @@ def time_case(case, steps, warmup, passes=1):
         pda.paged_decode_attn_timed(shape, plan, case.q, kc, vc, case.block_table,
                                     case.seq_lens_t, case.scale, out, ws, e0, e1)
 
-    for i in range(warmup):
+    # every replica pool is touched at least twice before timing (a pool's
+    # first use in a process pays for page-table and TLB set-up)
+    for i in range(max(warmup, 2 * R)):
         call(i)
     torch.cuda.synchronize()
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
