@@ -62,14 +62,45 @@ def log(msg):
 
 
 def replicas_for(case):
+    """KV pools the calls rotate through, so that no call finds the KV it reads
+    in the MALL or the L2s: at least ROTATE_BYTES of distinct attended KV lie
+    between two uses of one pool.  Returns (pools, block_table, num_blocks);
+    the pools share the table.  A sliding window reads a small part of the
+    case's pool, so its pools hold only the blocks the windows touch, in a
+    seeded random order (the table's other entries point at one of them and
+    are never read)."""
     import torch
-    pool = case.k_cache.numel() * case.k_cache.element_size() * 2
+    if case.sliding_window == 0:
+        pool = case.k_cache.numel() * case.k_cache.element_size() * 2
+        n = max(1, math.ceil(ROTATE_BYTES / pool))
+        reps = [(case.k_cache, case.v_cache)]
+        for _ in range(n - 1):
+            reps.append((case.k_cache.clone(), case.v_cache.clone()))
+        torch.cuda.synchronize()
+        return reps, case.block_table, case.num_blocks
+    table = case.block_table.cpu()
+    need = []
+    for b, L in enumerate(case.seq_lens):
+        if L > 0:
+            lo = max(0, L - case.sliding_window)
+            need += [(b, lb) for lb in range(lo // case.bs, (L - 1) // case.bs + 1)]
+    gen = torch.Generator()
+    gen.manual_seed(20240)
+    nb = len(need) + 1
+    perm = torch.randperm(nb, generator=gen)
+    idx = torch.zeros(nb, dtype=torch.int64)
+    new_table = torch.full_like(table, int(perm[-1]))
+    for i, (b, lb) in enumerate(need):
+        idx[perm[i]] = int(table[b, lb])
+        new_table[b, lb] = int(perm[i])
+    idx[perm[-1]] = int(table[need[0][0], need[0][1]]) if need else 0
+    idx = idx.to(case.k_cache.device)
+    kc, vc = case.k_cache[idx].contiguous(), case.v_cache[idx].contiguous()
+    pool = kc.numel() * kc.element_size() * 2
     n = max(1, math.ceil(ROTATE_BYTES / pool))
-    reps = [(case.k_cache, case.v_cache)]
-    for _ in range(n - 1):
-        reps.append((case.k_cache.clone(), case.v_cache.clone()))
+    reps = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n - 1)]
     torch.cuda.synchronize()
-    return reps
+    return reps, new_table.to(case.block_table.device), nb
 
 
 def time_case(case, steps, warmup, passes=1):
@@ -78,20 +109,20 @@ def time_case(case, steps, warmup, passes=1):
     passes in which the library attaches events to that launch.  Returns a
     dict with both, the plan and the last output."""
     import torch
+    import kvgen
     import paged_kv_cache_decode_amd as pda
-    shape = pda.make_shape(case.B, case.Hq, case.Hkv, case.D, case.bs, case.num_blocks,
-                           case.max_blocks_per_seq, case.max_seq_len, case.dtype)
+    reps, table, num_blocks = replicas_for(case)
+    R = len(reps)
+    shape = pda.make_shape(**dict(kvgen.shape_dict(case), num_blocks=num_blocks))
     plan = pda.paged_decode_attn_plan(shape)
     out = torch.empty_like(case.q)
     ws = torch.empty(max(1, pda.pda_workspace_bytes(shape, plan)), dtype=torch.uint8,
                      device=case.q.device)
     pda.paged_decode_attn_workspace_init(ws)
-    reps = replicas_for(case)
-    R = len(reps)
 
     def call(i, e0=None, e1=None):
         kc, vc = reps[i % R]
-        pda.paged_decode_attn_timed(shape, plan, case.q, kc, vc, case.block_table,
+        pda.paged_decode_attn_timed(shape, plan, case.q, kc, vc, table,
                                     case.seq_lens_t, case.scale, out, ws, e0, e1)
 
     # every replica pool is touched at least twice before timing (a pool's
@@ -140,6 +171,7 @@ def summary(name, case, r):
     kgbs = r["kv_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
     return {"workload": name, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv, "D": case.D,
             "block_size": case.bs, "dtype": case.dtype, "context_tokens": sum(case.seq_lens),
+            "sliding_window": case.sliding_window,
             "kv_bytes": r["kv_bytes"], "P": r["plan"].num_partitions,
             "T_p": r["plan"].tokens_per_partition, "us_per_call": round(us, 3),
             "splitkv_kernel_us": round(kus, 3), "GBps": round(gbs, 1),
@@ -192,7 +224,8 @@ def cpu_baseline(case, seconds):
     ref = None
     while t < seconds or n == 0:
         t0 = time.perf_counter()
-        ref = oracle.decode(q, k, v, lens, case.scale, nthreads=threads)
+        ref = oracle.decode(q, k, v, lens, case.scale, nthreads=threads,
+                            window=case.sliding_window)
         t += time.perf_counter() - t0
         n += 1
     per_call = t / n
@@ -257,6 +290,8 @@ def main():
         specs += [(f"cfg4 {n}", lambda n=n: configs.cfg4(n, device="cuda"))
                   for n in configs.CFG4_LENS]
         specs += [("cfg5 B64 mixed", lambda: configs.cfg5(device="cuda"))]
+        specs += [(f"cfg3 sliding W1024 B{b} 32K", lambda b=b: configs.cfg3_sliding(b, L, device="cuda"))
+                  for b in (1, 8)]
         for name, mk in specs:
             log(f"timing {name}")
             c = mk()

@@ -33,11 +33,21 @@
  *  - The return value is a status from host-side validation (PDA_OK or a
  *    negative PDA_ERR_*).  On an error nothing is launched.
  *
+ * Sliding window (pda_shape_t.sliding_window = W > 0): the softmax runs over
+ * the last W tokens only, t in [max(0, L - W), L) -- the sliding-window
+ * layers of page "vLLM's custom ROCm paged-attention kernel wins all sixty
+ * cells" (section 4, Figure 3: 1024-token scans).  Slots before the window
+ * are never read, like the unwritten tail: their rows are redirected to the
+ * window's first token and their scores are excluded by a select.  The
+ * partitions then tile [base, L) with base = max(0, L - W) rounded down to a
+ * multiple of 16, and the plan is sized for that span (see below).
+ *
  * Device-data contract (not checked on the hot path; violating it is
  * undefined behaviour):
  *  - 0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size;
  *  - block_table[b][j] is in [0, num_blocks) for j < ceil(seq_lens[b] / block_size);
- *    entries at or past that index are never read;
+ *    entries at or past that index are never read (with a sliding window,
+ *    neither are entries of blocks that end before the window);
  *  - K/V slots at or past seq_lens[b] may hold anything (NaN, Inf, garbage);
  *  - seq_lens[b] == 0 yields a zero output row.
  */
@@ -81,7 +91,9 @@ extern "C" {
 
 /* ---- the plan -------------------------------------------------------------
  * A pure integer function of (num_seqs B, num_kv_heads Hkv, G = Hq/Hkv,
- * head_size D, max_seq_len Lmax, compute-unit count C):
+ * head_size D, span Lmax, compute-unit count C), where the span is
+ * max_seq_len, or min(max_seq_len, W + 15) with a sliding window W > 0 (the
+ * window rounded out to the 16-token grid the partitions start on):
  *
  * Variant: MFMA if G > PDA_VALU_MAX_GROUP, or if G >= PDA_MFMA_MIN_GROUP and
  *   B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU load of the matrix cores
@@ -104,8 +116,8 @@ extern "C" {
  *   rounds.  (Every extra round, and every second workgroup on a CU, exposes
  *   a workgroup's start-up and epilogue again and doubles the partials the
  *   merge reads; one workgroup per CU measured fastest for both variants.)
- * Partition p of (b, g) covers tokens [p*T_p, min((p+1)*T_p, seq_lens[b]));
- * it is empty when p*T_p >= seq_lens[b].  The grid of the main kernel is
+ * Partition p of (b, g) covers tokens [base + p*T_p, min(base + (p+1)*T_p,
+ * seq_lens[b])), base = 0 without a window; it is empty when that range is.  The grid of the main kernel is
  * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
  * workspace is used; otherwise it writes fp32 partials that are merged with
  * the log-sum-exp rule, either
@@ -143,6 +155,7 @@ typedef struct pda_shape {
     int32_t max_blocks_per_seq;  /* MBS >= 1: row length of block_table */
     int32_t max_seq_len;         /* >= every seq_lens[b], <= MBS * bs; sizes the plan */
     int32_t dtype;               /* PDA_BF16 or PDA_FP16 */
+    int32_t sliding_window;      /* W >= 0; 0: attend to the whole context (see below) */
 } pda_shape_t;
 
 typedef struct pda_plan {
@@ -225,7 +238,8 @@ int paged_decode_attn_timed(const pda_shape_t* shape, const pda_plan_t* plan,
  *   trace_slot [B][Hkv][max_seq_len]  physical slot  block_id * bs + (t % bs)
  *   trace_part [B][Hkv][max_seq_len]  the partition p that consumed t
  * and for every unit trace_range [B][Hkv][P][2] = (t0, t1) (t1 <= t0 when the
- * partition is empty).  Entries for t >= seq_lens[b] are left untouched.
+ * partition is empty).  Entries for t >= seq_lens[b], and for t before a
+ * sliding window, are left untouched.
  * Device pointers; the caller pre-fills them with a sentinel. */
 int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan, int32_t rows,
                             const int32_t* block_table, const int32_t* seq_lens,

@@ -65,21 +65,27 @@ class Case:
     unref_ids: List[int] = field(default_factory=list)
     tail_k: str = "zero"
     tail_v: str = "zero"
+    sliding_window: int = 0         # W > 0: decode attends to the last W tokens
 
     @property
     def G(self) -> int:
         return self.Hq // self.Hkv
 
+    def attended(self, b: int) -> int:
+        """Tokens of sequence b the decode attends to."""
+        L = self.seq_lens[b]
+        return min(L, self.sliding_window) if self.sliding_window > 0 else L
+
     def kv_bytes(self) -> int:
-        """Algorithmic KV bytes: valid tokens only, K and V, 16-bit."""
-        return sum(self.seq_lens) * self.Hkv * self.D * 2 * 2
+        """Algorithmic KV bytes: attended tokens only, K and V, 16-bit."""
+        return sum(self.attended(b) for b in range(self.B)) * self.Hkv * self.D * 2 * 2
 
 
 def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int],
               dtype: str = "bf16", seed: int = 0, device="cpu", extra_blocks: int = 1,
               max_blocks_per_seq: Optional[int] = None, tail_k: str = "zero",
               tail_v: str = "zero", scale: Optional[float] = None,
-              max_seq_len: Optional[int] = None) -> Case:
+              max_seq_len: Optional[int] = None, sliding_window: int = 0) -> Case:
     assert len(seq_lens) == B and Hq % Hkv == 0
     tdt = _DT[dtype]
     device = torch.device(device)
@@ -109,7 +115,8 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
                 scale=float(scale) if scale is not None else D ** -0.5,
                 num_blocks=NB, max_blocks_per_seq=MBS,
                 max_seq_len=int(max_seq_len) if max_seq_len is not None else max(lens),
-                unref_ids=unref, tail_k=tail_k, tail_v=tail_v)
+                unref_ids=unref, tail_k=tail_k, tail_v=tail_v,
+                sliding_window=int(sliding_window))
     return page(case, tail_k=tail_k, tail_v=tail_v)
 
 
@@ -158,6 +165,26 @@ def repermute(case: Case, seed: int) -> Case:
     return page(case, tail_k=case.tail_k, tail_v=case.tail_v, block_table=table, unref_ids=unref)
 
 
+def poison_before_window(case: Case, fill: str = "nan") -> Case:
+    """The same case with the cache slots of every token before its sequence's
+    sliding window (t < L_b - W) overwritten with `fill`: tokens the decode
+    must not read."""
+    assert case.sliding_window > 0
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    table = case.block_table.cpu().to(torch.int64)
+    for b in range(case.B):
+        lo = max(0, case.seq_lens[b] - case.sliding_window)
+        if lo == 0:
+            continue
+        t = torch.arange(lo)
+        blocks = table[b, t // case.bs].to(kc.device)
+        slots = (t % case.bs).to(kc.device)
+        for h in range(case.Hkv):
+            kc[blocks, h, slots] = _TAIL[fill]
+            vc[blocks, h, slots] = _TAIL[fill]
+    return replace(case, k_cache=kc, v_cache=vc)
+
+
 def oracle_inputs(case: Case, seqs: Optional[Sequence[int]] = None):
     """fp32 numpy inputs for the oracle (exact upcasts), optionally for a
     subset of sequences (re-indexed 0..len(seqs)-1)."""
@@ -173,4 +200,4 @@ def shape_dict(case: Case) -> dict:
     return dict(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
                 head_size=case.D, block_size=case.bs, num_blocks=case.num_blocks,
                 max_blocks_per_seq=case.max_blocks_per_seq, max_seq_len=case.max_seq_len,
-                dtype=case.dtype)
+                dtype=case.dtype, sliding_window=case.sliding_window)

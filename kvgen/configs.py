@@ -9,6 +9,8 @@
   cfg3  gemma-3-27B-like layer: Hq 32 / Hkv 16, D 128, bs 16, B 1 or 8,
         L in 1K..32K plus lengths that straddle the final tile; bf16 and
         fp16; NaN tails in K, V or both (same page, section 5, Figure 4).
+        Its sliding layers (cfg3_sliding) attend to the last 1024 tokens only
+        (same page, section 4, Figure 3).
   cfg4  low-parallelism layer: B 1, Hq 24 / Hkv 4 (ratio 6), D 256, block
         size 784 = 16 x 49 (page "Hybrid-SSM decode rate on dual Radeon
         cards", the gate passage), L {500, 1K, 4K, 8K, 16K, 24K, 32K}.
@@ -44,6 +46,13 @@ def cfg3(B: int, L: int, dtype: str = "bf16", device="cpu", tail_k: str = "nan",
     return make_case(B=B, Hq=32, Hkv=16, D=128, bs=16, seq_lens=[L] * B, dtype=dtype,
                      seed=seed_for(3, cell), device=device, extra_blocks=1,
                      tail_k=tail_k, tail_v=tail_v)
+
+
+def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu",
+                 tail: str = "nan", cell: int = 0) -> Case:
+    return make_case(B=B, Hq=32, Hkv=16, D=128, bs=16, seq_lens=[L] * B, dtype=dtype,
+                     seed=seed_for(3, 100 + cell), device=device, extra_blocks=1,
+                     tail_k=tail, tail_v=tail, sliding_window=W)
 
 
 def cfg4(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:

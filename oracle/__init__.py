@@ -8,6 +8,8 @@ and never imports it; the GPU library never imports this package.
 Contents
   decode / decode_rows / partial   fp32 two-pass softmax(q K^T * scale) V over
                                    the contiguous, pre-paging K/V tensors
+                                   (optionally over each sequence's last W
+                                   tokens: a sliding window)
                                    (oracle.c, via ctypes).  The pages fix the
                                    reference at fp32 computed from pre-paging
                                    KV (page "vLLM's custom ROCm paged-attention
@@ -98,9 +100,24 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def decode(q, k, v, seq_lens, scale, nthreads: int = 0) -> np.ndarray:
+def _window(k, v, seq_lens, window: int):
+    """Restrict each sequence to its last `window` tokens (window > 0): the
+    sliding-window layers attend to t in [max(0, L - W), L) (page "vLLM's
+    custom ROCm paged-attention kernel wins all sixty cells", section 4,
+    Figure 3).  window == 0 keeps the whole context."""
+    if window <= 0:
+        return k, v, seq_lens
+    lens = [int(L) for L in seq_lens]
+    lo = [max(0, L - window) for L in lens]
+    k = [np.asarray(k[b])[:, lo[b]:lens[b]] for b in range(len(lens))]
+    v = [np.asarray(v[b])[:, lo[b]:lens[b]] for b in range(len(lens))]
+    return k, v, [lens[b] - lo[b] for b in range(len(lens))]
+
+
+def decode(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.ndarray:
     """All rows: float32 [B, Hq, D]."""
     lib = _load()
+    k, v, seq_lens = _window(k, v, seq_lens, window)
     pk = _Packed(q, k, v, seq_lens)
     out = np.empty((pk.B, pk.Hq, pk.D), dtype=np.float32)
     rc = lib.oracle_decode(pk.B, pk.Hq, pk.Hkv, pk.D, _ptr(pk.seq_lens), _ptr(pk.kv_off),
@@ -111,9 +128,10 @@ def decode(q, k, v, seq_lens, scale, nthreads: int = 0) -> np.ndarray:
     return out
 
 
-def decode_rows(q, k, v, seq_lens, scale, rows, nthreads: int = 0) -> np.ndarray:
+def decode_rows(q, k, v, seq_lens, scale, rows, nthreads: int = 0, window: int = 0) -> np.ndarray:
     """Selected (b, h) rows: float32 [len(rows), D]."""
     lib = _load()
+    k, v, seq_lens = _window(k, v, seq_lens, window)
     pk = _Packed(q, k, v, seq_lens)
     rows = list(rows)
     rb = np.ascontiguousarray([r[0] for r in rows], dtype=np.int32)

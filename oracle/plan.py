@@ -43,19 +43,27 @@ def token_bounds(head_size: int):
     return t_min, t_many, t_one
 
 
+def span(max_seq_len: int, window: int = 0) -> int:
+    """Tokens the partitions must cover: max_seq_len, or with a sliding
+    window W > 0 at most W + 15 (the window, from its first token rounded
+    down to a multiple of 16)."""
+    return min(max_seq_len, window + 15) if window > 0 else max_seq_len
+
+
 def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_seq_len: int,
-              cu_count: int):
+              cu_count: int, window: int = 0):
     """(P, T_p, variant) for the documented rule."""
     var = variant(num_seqs, num_kv_heads, group)
     t_min, t_many, t_one = token_bounds(head_size)
     units = num_seqs * num_kv_heads
     p_fill = _cdiv(cu_count, units)
-    if max_seq_len <= 0:
+    lspan = span(max_seq_len, window)
+    if lspan <= 0:
         t_p = t_min
     else:
-        t_fill = max(t_min, _cdiv(_cdiv(max_seq_len, p_fill), TP_ALIGN) * TP_ALIGN)
+        t_fill = max(t_min, _cdiv(_cdiv(lspan, p_fill), TP_ALIGN) * TP_ALIGN)
         t_p = t_fill if t_fill <= t_one else t_many
-    p = max(1, _cdiv(max_seq_len, t_p))
+    p = max(1, _cdiv(lspan, t_p))
     return p, t_p, var
 
 

@@ -40,7 +40,7 @@ class PdaShape(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("sliding_window", ctypes.c_int32)]
 
 
 class PdaPlan(ctypes.Structure):
@@ -103,14 +103,16 @@ def load_library():
 
 
 def make_shape(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
-               max_blocks_per_seq, max_seq_len, dtype="bf16") -> PdaShape:
+               max_blocks_per_seq, max_seq_len, dtype="bf16", sliding_window=0) -> PdaShape:
+    """sliding_window W > 0: attend to the last W tokens of each sequence."""
     dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     return PdaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_size),
                     int(block_size), int(num_blocks), int(max_blocks_per_seq), int(max_seq_len),
-                    dt)
+                    dt, int(sliding_window))
 
 
-def shape_from_tensors(q, k_cache, block_table, max_seq_len: int) -> PdaShape:
+def shape_from_tensors(q, k_cache, block_table, max_seq_len: int,
+                       sliding_window: int = 0) -> PdaShape:
     import torch
     B, Hq, D = q.shape
     NB, Hkv, bs, D2 = k_cache.shape
@@ -119,7 +121,8 @@ def shape_from_tensors(q, k_cache, block_table, max_seq_len: int) -> PdaShape:
     dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(q.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    return make_shape(B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seq_len, dt)
+    return make_shape(B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seq_len, dt,
+                      sliding_window)
 
 
 def pda_status_string(status: int) -> str:
@@ -194,13 +197,14 @@ def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
 
 def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, out=None,
                       workspace=None, max_seq_len: Optional[int] = None, plan: Optional[PdaPlan] = None,
-                      stream=None):
+                      stream=None, sliding_window: int = 0):
     """Decode one query token per sequence over the paged KV cache.
 
     q [B, Hq, D], k_cache/v_cache [NB, Hkv, bs, D] (bf16 or fp16, one dtype),
     block_table [B, MBS] int32, seq_lens [B] int32, all on the current device.
     max_seq_len must bound every seq_lens entry (default: block_table width *
-    block size, which is always valid but may over-partition).  Returns `out`.
+    block size, which is always valid but may over-partition).
+    sliding_window W > 0 attends to the last W tokens only.  Returns `out`.
     """
     import torch
     if out is None:
@@ -208,7 +212,7 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
     _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out)
     if max_seq_len is None:
         max_seq_len = block_table.shape[1] * k_cache.shape[2]
-    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len)
+    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window)
     lib = load_library()
     if plan is None:
         need = paged_decode_attn_workspace_size(shape)
@@ -233,10 +237,11 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
 
 def paged_decode_attn_with_plan(q, k_cache, v_cache, block_table, seq_lens, scale: float,
                                 plan: PdaPlan, out=None, workspace=None,
-                                max_seq_len: Optional[int] = None, stream=None):
+                                max_seq_len: Optional[int] = None, stream=None,
+                                sliding_window: int = 0):
     return paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale, out=out,
                              workspace=workspace, max_seq_len=max_seq_len, plan=plan,
-                             stream=stream)
+                             stream=stream, sliding_window=sliding_window)
 
 
 def paged_decode_attn_workspace_init(workspace, stream=None):

@@ -64,6 +64,7 @@ struct DecodeParams {
     int32_t block_size;        // bs
     int32_t max_blocks_per_seq;// MBS
     int32_t max_seq_len;       // host bound on seq_lens (also the trace row length)
+    int32_t window;            // sliding window W (0: whole context)
     int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
     int32_t num_partitions;    // P
     int32_t tokens_per_part;   // T_p

@@ -101,8 +101,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int q4 = lane >> 4, c16 = lane & 15;
     const int G = p.group;
-    const int L = context_len(p, b);
-    const int t0 = part * p.tokens_per_part;
+    const SeqRange rg = seq_range(p, b);
+    const int L = rg.L;
+    const int t0 = rg.base + part * p.tokens_per_part;
     const bool direct = p.num_partitions == 1;
 
     if (t0 >= L) {  // empty partition; the first one of an empty context writes zeros
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const bool valid = jj < ntiles;
         const int tile_base = t0 + min(jj, ntiles - 1) * TT;
         int phys, slot0, dt;
-        locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, mfma_k_offset(lane), phys, slot0, dt);
+        locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, mfma_k_offset(lane), phys, slot0,
+                            dt);
         {
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + k_lane;
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, mfma_v_offset(lane, r), phys, slot0,
-                                dt);
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, mfma_v_offset(lane, r), phys,
+                                slot0, dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + v_lane;
 #pragma unroll
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 
     auto process = [&](int j, const uint4 (&kr)[KS], const uint4 (&vr)[4][DH]) {
         const int tile_base = t0 + j * TT;
-        const bool full = tile_base + TT <= t1;
+        const bool full = tile_base >= rg.lo && tile_base + TT <= t1;
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(kr[s], qb[s], sacc);
@@ -194,8 +196,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * p.scale_log2;
         if (!full) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sc[r] = tile_base + mfma_v_offset(lane, r) < t1 ? sc[r] : -INFINITY;
+            for (int r = 0; r < 4; ++r) {
+                const int t = tile_base + mfma_v_offset(lane, r);
+                sc[r] = (t >= rg.lo && t < t1) ? sc[r] : -INFINITY;
+            }
         }
         float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         write_unit_rows<Elt, D>(p, red, kHeadChunk, h0, hn, b, g, part);
         if (h0 + kHeadChunk < G) __syncthreads();  // before the next chunk reuses red
     }
-    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, L, b, g);
+    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
 
 #if PDA_DTYPE == 0

@@ -56,8 +56,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int c = lane % LPT, r = lane / LPT;
     const int G = p.group;
-    const int L = context_len(p, b);
-    const int t0 = part * p.tokens_per_part;
+    const SeqRange rg = seq_range(p, b);
+    const int L = rg.L;
+    const int t0 = rg.base + part * p.tokens_per_part;
     const bool direct = p.num_partitions == 1;
 
     if (t0 >= L) {  // empty partition; the first one of an empty context writes zeros
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int phys, slot0, dt;
-            locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, t1, u, r, phys, slot0, dt);
+            locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0, dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + lane_off;
             if constexpr (kBuf) {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // One tile of QK^T, masking, online softmax and PV for this lane.
     auto process = [&](int j, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
         const int tile_base = t0 + j * TT;
-        const bool full = tile_base + TT <= t1;
+        const bool full = tile_base >= rg.lo && tile_base + TT <= t1;
         float s[U][GP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -146,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         if (!full) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool valid = tile_base + u * R + r < t1;
+                const int t = tile_base + u * R + r;
+                const bool valid = t >= rg.lo && t < t1;
 #pragma unroll
                 for (int i = 0; i < GP; ++i) s[u][i] = valid ? s[u][i] : -INFINITY;
             }
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 
     // merge the wavefronts and write the unit's result
     write_unit_rows<Elt, D>(p, red, GP, 0, G, b, g, part);
-    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, L, b, g);
+    if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
 
 #if PDA_DTYPE == 0

@@ -179,10 +179,30 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
     return max(0, min(p.seq_lens[b], p.max_seq_len));
 }
 
+// Tokens of sequence b the decode attends to: [lo, L), lo = max(0, L - W)
+// for a sliding window W > 0, else 0.  The partitions tile [base, L) with
+// base = lo rounded down to the 16-token grid, so that aligned tiles keep
+// starting on it; rows in [base, lo) are redirected to lo (locate_row) and
+// their scores are masked, so no slot before the window is ever read.
+struct SeqRange {
+    int L, lo, base;
+};
+__device__ inline SeqRange seq_range(const DecodeParams& p, int b) {
+    const int L = context_len(p, b);
+    const int lo = p.window > 0 ? max(0, L - p.window) : 0;
+    return SeqRange{L, lo, lo & ~(kAlignTokens - 1)};
+}
+
+// Partitions of a unit that hold tokens (the rest are empty).
+__device__ inline int live_partitions(const DecodeParams& p, const SeqRange& r) {
+    return min(p.num_partitions, (r.L - r.base + p.tokens_per_part - 1) / p.tokens_per_part);
+}
+
 // Physical block and slot of the row a lane reads: the token at in-tile
 // offset `o` of the tile starting at tile_base, slot = slot0 + dt.  Tokens at
 // or past t1 (the partition end, never past the sequence end) are redirected
-// to token t1-1, so no slot at or past seq_len is ever addressed.  Block ids
+// to token t1-1, and tokens before lo (the first token attended to) to lo,
+// so no slot past seq_len or before a sliding window is ever addressed.  Block ids
 // are clamped into the pool, so a corrupt table entry gives a wrong row,
 // never an access outside the pool.
 //  ALIGNED (block size a multiple of 16, tiles starting at multiples of 16
@@ -196,12 +216,12 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
 //  lane divides its own token index by the block size and dt = 0.
 template <bool ALIGNED>
 __device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int lb0,
-                                  int tile_base, int t1, int o0, int o, int& phys, int& slot0,
-                                  int& dt) {
-    const int last = t1 - 1 - tile_base;
-    const int t = tile_base + min(o, last);
+                                  int tile_base, int lo, int t1, int o0, int o, int& phys,
+                                  int& slot0, int& dt) {
+    const int first = lo - tile_base, last = t1 - 1 - tile_base;
+    const int t = tile_base + min(max(o, first), last);
     if constexpr (ALIGNED) {
-        const int ub = tile_base + min(o0, last);
+        const int ub = tile_base + min(max(o0, first), last);
         const int lb = (int)fastdiv((uint32_t)ub, p.bs_div);
         slot0 = ub - lb * p.block_size;
         dt = t - ub;
@@ -220,9 +240,9 @@ __device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int
 // R divides 16 and rounds start at multiples of R).
 template <int R, bool ALIGNED>
 __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, int lb0,
-                                    int tile_base, int t1, int u, int r, int& phys, int& slot0,
-                                    int& dt) {
-    locate_row<ALIGNED>(p, tbl, lb0, tile_base, t1, u * R, u * R + r, phys, slot0, dt);
+                                    int tile_base, int lo, int t1, int u, int r, int& phys,
+                                    int& slot0, int& dt) {
+    locate_row<ALIGNED>(p, tbl, lb0, tile_base, lo, t1, u * R, u * R + r, phys, slot0, dt);
 }
 
 // ---- MFMA tile geometry --------------------------------------------------
@@ -320,11 +340,12 @@ __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
 // counter for the next call and reads the partials back with device-scope
 // loads.  No L2 write-back or invalidate is needed.
 template <typename Elt, int D>
-__device__ inline void fused_merge_tail(const DecodeParams& p, int L, int b, int g) {
+__device__ inline void fused_merge_tail(const DecodeParams& p, const SeqRange& rg, int b,
+                                        int g) {
     __shared__ int s_last;
     wait_stores_done();
     __syncthreads();
-    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
+    const int Pb = live_partitions(p, rg);
     if (threadIdx.x == 0) {
         int32_t* ctr = p.counters + (int64_t)b * p.num_kv_heads + g;
         const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

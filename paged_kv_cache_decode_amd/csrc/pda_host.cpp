@@ -84,12 +84,20 @@ int64_t table_capacity(const pda_shape_t* s, const pda_plan_t* pl) {
     return (int64_t)pl->tokens_per_partition / s->block_size + 2;
 }
 
+// Tokens a partition grid must cover: the whole context, or a sliding
+// window rounded out to the 16-token grid its partitions start on.
+int64_t plan_span(const pda_shape_t* s) {
+    if (s->sliding_window > 0)
+        return std::min<int64_t>(s->max_seq_len, (int64_t)s->sliding_window + kAlignTokens - 1);
+    return s->max_seq_len;
+}
+
 int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
     if (!pl) return PDA_ERR_INVALID;
     if (pl->num_partitions < 1 || pl->tokens_per_partition < PDA_TP_ALIGN ||
         pl->tokens_per_partition % PDA_TP_ALIGN != 0)
         return PDA_ERR_INVALID;
-    if ((int64_t)pl->num_partitions * pl->tokens_per_partition < (int64_t)s->max_seq_len)
+    if ((int64_t)pl->num_partitions * pl->tokens_per_partition < plan_span(s))
         return PDA_ERR_INVALID;
     if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen)
         return PDA_ERR_UNSUPPORTED;
@@ -135,6 +143,7 @@ DecodeParams make_params(const pda_shape_t* s, const pda_plan_t* pl, float scale
     p.block_size = s->block_size;
     p.max_blocks_per_seq = s->max_blocks_per_seq;
     p.max_seq_len = s->max_seq_len;
+    p.window = s->sliding_window;
     p.num_blocks = s->num_blocks;
     p.num_partitions = pl->num_partitions;
     p.tokens_per_part = pl->tokens_per_partition;
@@ -155,7 +164,8 @@ extern "C" {
 int pda_check_shape(const pda_shape_t* s) {
     if (!s) return PDA_ERR_INVALID;
     if (s->num_seqs < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->block_size < 1 ||
-        s->num_blocks < 1 || s->max_blocks_per_seq < 1 || s->max_seq_len < 0)
+        s->num_blocks < 1 || s->max_blocks_per_seq < 1 || s->max_seq_len < 0 ||
+        s->sliding_window < 0)
         return PDA_ERR_INVALID;
     if (s->num_q_heads % s->num_kv_heads != 0) return PDA_ERR_INVALID;
     if (s->head_size != 64 && s->head_size != 128 && s->head_size != 256)
@@ -187,11 +197,12 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     const int64_t t_one = std::max(t_many, (PDA_WG_ONE_BYTES / bpt / align) * align);
     const int64_t p_fill = cdiv64(cu_count, units);
     int64_t tp = t_min;
-    if (s->max_seq_len > 0) {
-        const int64_t t_fill = std::max(t_min, cdiv64(cdiv64(s->max_seq_len, p_fill), align) * align);
+    const int64_t span = plan_span(s);
+    if (span > 0) {
+        const int64_t t_fill = std::max(t_min, cdiv64(cdiv64(span, p_fill), align) * align);
         tp = t_fill <= t_one ? t_fill : t_many;
     }
-    int64_t P = cdiv64(s->max_seq_len, tp);
+    int64_t P = cdiv64(span, tp);
     if (P < 1) P = 1;
     plan->num_partitions = (int32_t)P;
     plan->tokens_per_partition = (int32_t)tp;

@@ -49,8 +49,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
             }
         }
     }
-    const int L = context_len(p, b);
-    const int Pb = min(p.num_partitions, (L + p.tokens_per_part - 1) / p.tokens_per_part);
+    const int Pb = live_partitions(p, seq_range(p, b));
     if constexpr (!AHEAD) {
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {

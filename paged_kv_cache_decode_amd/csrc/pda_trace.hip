@@ -22,8 +22,9 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane % LPT, r = lane / LPT;
-    const int L = context_len(p, b);
-    const int t0 = part * p.tokens_per_part;
+    const SeqRange rg = seq_range(p, b);
+    const int L = rg.L;
+    const int t0 = rg.base + part * p.tokens_per_part;
     const int t1 = min(t0 + p.tokens_per_part, L);
     const int64_t unit = (int64_t)b * p.num_kv_heads + g;
     if (threadIdx.x == 0) {
@@ -51,20 +52,23 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
         if constexpr (ROWS == 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, t1, u, r, phys, slot0, dt);
+                locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0,
+                                         dt);
                 const int t = tile_base + u * R + r;
-                if (c == 0 && t < t1) record(t, phys, slot0 + dt);
+                if (c == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
         } else if constexpr (ROWS == 1) {
             const int o = mfma_k_offset(lane);
-            locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, o, phys, slot0, dt);
-            if ((lane >> 4) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, o, phys, slot0, dt);
+            const int t = tile_base + o;
+            if ((lane >> 4) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int o = mfma_v_offset(lane, rr);
-                locate_row<ALIGNED>(p, tv, tlb0, tile_base, t1, 0, o, phys, slot0, dt);
-                if ((lane & 15) == 0 && tile_base + o < t1) record(tile_base + o, phys, slot0 + dt);
+                locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, o, phys, slot0, dt);
+                const int t = tile_base + o;
+                if ((lane & 15) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
         }
     }

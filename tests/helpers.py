@@ -26,14 +26,15 @@ def shape_of(case: kvgen.Case) -> pda.PdaShape:
 def run(case: kvgen.Case, plan=None, out=None) -> torch.Tensor:
     out = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                 case.seq_lens_t, case.scale, out=out,
-                                max_seq_len=case.max_seq_len, plan=plan)
+                                max_seq_len=case.max_seq_len, plan=plan,
+                                sliding_window=case.sliding_window)
     torch.cuda.synchronize()
     return out
 
 
 def reference(case: kvgen.Case, seqs=None) -> np.ndarray:
     q, k, v, lens = kvgen.oracle_inputs(case, seqs)
-    return oracle.decode(q, k, v, lens, case.scale)
+    return oracle.decode(q, k, v, lens, case.scale, window=case.sliding_window)
 
 
 def check(case: kvgen.Case, got: torch.Tensor, ref: np.ndarray = None, seqs=None,

@@ -49,9 +49,10 @@ def test_plan_matches_oracle_plan(D):
         L = int(rng.integers(0, 300000))
         mbs = max(1, -(-L // bs))
         cu = int(rng.choice([1, 7, 80, 256, 304]))
-        shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16")
+        W = int(rng.choice([0, 0, 1, 31, 1024]))
+        shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16", sliding_window=W)
         got = pda.pda_plan_for_cus(shape, cu)
-        P, T, var = oplan.partition(B, Hkv, G, D, L, cu)
+        P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W)
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
         assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv)
         assert got.merge == pda.PDA_MERGE_KERNEL
@@ -64,7 +65,8 @@ def test_plan_golden_through_library():
         g = json.load(f)
     for c in g["cases"]:
         shape = pda.make_shape(c["B"], c["Hkv"] * c["G"], c["Hkv"], c["D"], 16, 1,
-                               max(1, -(-c["Lmax"] // 16)), c["Lmax"])
+                               max(1, -(-c["Lmax"] // 16)), c["Lmax"],
+                               sliding_window=c.get("W", 0))
         got = pda.pda_plan_for_cus(shape, g["cu_count"])
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == \
             (c["P"], c["T_p"], c["variant"]), c["name"]
@@ -81,6 +83,7 @@ BAD_SHAPES = [
     (dict(max_seq_len=-1), pda.PDA_ERR_INVALID),
     (dict(max_seq_len=16 * 4 + 1), pda.PDA_ERR_INVALID),  # > MBS * bs
     (dict(num_blocks=0), pda.PDA_ERR_INVALID),
+    (dict(sliding_window=-1), pda.PDA_ERR_INVALID),
 ]
 
 

@@ -206,3 +206,58 @@ def test_metric_floor_of_output_rounding(dtype, bound):
     rounded = torch.from_numpy(ref).to(tdt).float().numpy()
     err = oracle.rel_linf(rounded, ref)
     assert bound / 4 < err <= bound
+
+
+# ---- sliding window (the sliding layers of page "vLLM's custom ROCm
+# paged-attention kernel wins all sixty cells", section 4, Figure 3) -------
+
+def sdpa_f64_masked(q, k, v, lens, scale, window):
+    """torch SDPA in float64 over each sequence's whole context with a key
+    mask that keeps t >= L - W: the window fixed by masking, not by slicing
+    (the oracle slices)."""
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = lens[b]
+        if L == 0:
+            continue
+        qt = torch.from_numpy(np.asarray(q[b], dtype=np.float64))[None, :, None, :]
+        kt = torch.from_numpy(np.asarray(k[b], dtype=np.float64))[None]
+        vt = torch.from_numpy(np.asarray(v[b], dtype=np.float64))[None]
+        keep = (torch.arange(L) >= L - window)[None, :]     # [1 query, L keys]
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=keep,
+                                                              scale=scale, enable_gqa=True)
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("lens,W", [([40, 33], 1), ([40, 33], 17), ([40, 33], 40),
+                                    ([40, 33], 64), ([100, 57], 33), ([64, 48], 16),
+                                    ([300, 1], 129)])
+def test_window_matches_masked_sdpa(lens, W):
+    case = kvgen.make_case(2, 8, 2, 64, 16, lens, seed=7 + W, sliding_window=W)
+    q, k, v, L = kvgen.oracle_inputs(case)
+    got = oracle.decode(q, k, v, L, case.scale, window=W)
+    ref = sdpa_f64_masked(q, k, v, L, case.scale, W)
+    assert oracle.rel_linf(got, ref) <= 1e-5
+    # and a window changes the result whenever it cuts the context
+    full = oracle.decode(q, k, v, L, case.scale)
+    if W < max(lens):
+        assert oracle.rel_linf(got, full) > 1e-3
+
+
+def test_window_of_one_token_is_the_last_v_row():
+    case = kvgen.make_case(2, 4, 2, 128, 16, [37, 9], seed=11, sliding_window=1)
+    q, k, v, L = kvgen.oracle_inputs(case)
+    got = oracle.decode(q, k, v, L, case.scale, window=1)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(got[b, h], v[b][h // 2, L[b] - 1])
+
+
+def test_window_covering_the_context_is_the_full_decode():
+    case = kvgen.make_case(2, 8, 4, 128, 16, [40, 17], seed=12)
+    q, k, v, L = kvgen.oracle_inputs(case)
+    full = oracle.decode(q, k, v, L, case.scale)
+    for W in (40, 41, 1000):
+        assert np.array_equal(oracle.decode(q, k, v, L, case.scale, window=W), full)

@@ -17,7 +17,8 @@ def test_plan_hand_derived_values():
     with open(GOLDEN) as f:
         g = json.load(f)
     for c in g["cases"]:
-        P, T, var = plan.partition(c["B"], c["Hkv"], c["G"], c["D"], c["Lmax"], g["cu_count"])
+        P, T, var = plan.partition(c["B"], c["Hkv"], c["G"], c["D"], c["Lmax"], g["cu_count"],
+                                   window=c.get("W", 0))
         assert (P, T, var) == (c["P"], c["T_p"], c["variant"]), c["name"]
 
 
@@ -31,11 +32,15 @@ def test_plan_invariants(D):
         G = int(rng.integers(1, 17))
         L = int(rng.integers(0, 200000))
         cu = int(rng.choice([1, 80, 104, 256, 304]))
-        P, T, var = plan.partition(B, Hkv, G, D, L, cu)
+        W = int(rng.choice([0, 0, 1, 17, 1024, 4096]))
+        P, T, var = plan.partition(B, Hkv, G, D, L, cu, window=W)
+        S = plan.span(L, W)
+        assert S <= L and (W == 0 or S <= W + 15)
         assert T % plan.TP_ALIGN == 0 and t_min <= T <= t_one
-        assert P >= 1 and P * T >= L
+        assert P >= 1 and P * T >= S
+        L = S
         if L > 0:
-            assert (P - 1) * T < L          # no partition is empty at Lmax
+            assert (P - 1) * T < L          # no partition is empty at the span
             # either one round of one workgroup per CU covers the job, or the
             # partitions are T_many
             assert P * B * Hkv <= cu + B * Hkv or T == t_many
@@ -66,3 +71,23 @@ def test_expected_trace_matches_token_loop():
             for p in range(P):
                 t0, t1 = ranges[b, g, p]
                 assert t0 == p * T and t1 == min(p * T + T, L)
+
+
+def test_expected_trace_with_window_matches_token_loop():
+    W = 21
+    case = kvgen.make_case(3, 8, 2, 64, 5, [0, 23, 61], seed=44, extra_blocks=2, sliding_window=W)
+    P, T = 1, 64   # span min(61, 36) = 36 tokens: one 64-token partition
+    slot, part, ranges, valid = bookkeeping.expected_trace(
+        case.block_table.numpy(), case.seq_lens, 2, case.bs, 64, P, T, window=W)
+    table = case.block_table.numpy()
+    for b in range(3):
+        L = case.seq_lens[b]
+        lo = max(0, L - W)
+        base = lo - lo % 16
+        for g in range(2):
+            for t in range(64):
+                assert valid[b, g, t] == (lo <= t < L)
+                if lo <= t < L:
+                    assert slot[b, g, t] == table[b][t // 5] * 5 + t % 5
+                    assert part[b, g, t] == (t - base) // T
+            assert tuple(ranges[b, g, 0]) == (base, min(base + T, L))
