@@ -54,6 +54,10 @@ WORKLOADS = {
     "cfg5": dict(make=lambda: _cfg().cfg5(device="cuda"),
                  desc="mixed-length decode, batch 64, 32 query / 8 KV heads, head 128, "
                       "block 16, contexts U[1K, 32K], bf16 KV ~N(0,1), fragmented tables"),
+    "sliding-B8-32K": dict(make=lambda: _cfg().cfg3_sliding(8, 32768, device="cuda"),
+                           desc="gemma-like sliding layer, batch 8, 32 query / 16 KV heads, "
+                                "head 128, block 16, 32768-token contexts, 1024-token window, "
+                                "bf16 KV ~N(0,1)"),
 }
 
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "pda.h"
@@ -45,11 +46,21 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
 
 // Everything one decode launch needs; passed by value as the kernel argument.
 struct DecodeParams {
+    // what a decode workgroup needs first (its first table entries and the
+    // context length) fills the first 64 bytes, which one scalar load brings
     const void* q;             // [B][Hq][D]
-    const void* k_cache;       // [NB][Hkv][bs][D]
-    const void* v_cache;       // [NB][Hkv][bs][D]
     const int32_t* block_table;// [B][MBS]
     const int32_t* seq_lens;   // [B]
+    int32_t tokens_per_part;   // T_p
+    int32_t max_blocks_per_seq;// MBS
+    FastDiv bs_div;
+    int32_t group;             // G = Hq / Hkv
+    int32_t num_q_heads;       // Hq
+    int32_t max_seq_len;       // host bound on seq_lens (also the trace row length)
+    int32_t window;            // sliding window W (0: whole context)
+    int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
+    const void* k_cache;       // [NB][Hkv][bs][D]
+    const void* v_cache;       // [NB][Hkv][bs][D]
     void* out;                 // [B][Hq][D]
     float* ws_o;               // [B][Hq][P][D]    (P > 1 only)
     float* ws_ml;              // [B][Hq][P][2]    (P > 1 only)
@@ -58,22 +69,16 @@ struct DecodeParams {
     int32_t* trace_part;
     int32_t* trace_range;
     float scale_log2;          // scale * log2(e): scores live in the exp2 domain
-    int32_t num_q_heads;       // Hq
     int32_t num_kv_heads;      // Hkv
-    int32_t group;             // G = Hq / Hkv
     int32_t block_size;        // bs
-    int32_t max_blocks_per_seq;// MBS
-    int32_t max_seq_len;       // host bound on seq_lens (also the trace row length)
-    int32_t window;            // sliding window W (0: whole context)
-    int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
     int32_t num_partitions;    // P
-    int32_t tokens_per_part;   // T_p
     int32_t tbl_capacity;      // LDS entries reserved for the block-table slice
     int32_t fused_merge;       // 1: the last unit of each (b, g) merges the partials
-    FastDiv bs_div;
     int64_t block_stride;      // Hkv * bs * D elements
     int32_t head_stride;       // bs * D elements
 };
+static_assert(offsetof(DecodeParams, num_blocks) + sizeof(int32_t) <= 64,
+              "the start-up fields fit one 64-byte scalar load");
 
 constexpr int kWave = 64;
 // Wavefronts per workgroup of the decode kernels (tiles of a partition are

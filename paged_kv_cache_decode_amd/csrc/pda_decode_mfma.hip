@@ -101,7 +101,35 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int q4 = lane >> 4, c16 = lane & 15;
     const int G = p.group;
-    const SeqRange rg = seq_range(p, b);
+
+    // Loads that do not depend on the context length leave together with the
+    // seq_lens load, so the first K/V loads wait for one round trip, not three:
+    // Q^T, the B operand (head c16 of the group, elements 32s + 8*q4 .. +8 for
+    // k-step s; lanes past G read head G-1 again, and the results of those
+    // padding heads are never written), and on the aligned path the table
+    // entries of the wave's first two tiles at the partition's start without
+    // a sliding window.
+    const int raw_len = p.seq_lens[b];
+    uint4 qb[KS];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                               ((int64_t)b * p.num_q_heads + g * G + min(c16, G - 1)) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qb[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+    }
+    const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+    TileBlock first[2] = {{0, 0}, {0, 0}};
+    if constexpr (ALIGNED) {
+        const int ts = part * p.tokens_per_part + wave * TT;
+        const int lb0 = tile_table_index(p, ts), lb1 = tile_table_index(p, ts + kWaves * TT);
+        const int e0 = table_entry(trow, lb0), e1 = table_entry(trow, lb1);
+        keep_issued(raw_len, e0, e1);
+        first[0] = tile_block_of(p, e0, lb0, ts);
+        first[1] = tile_block_of(p, e1, lb1, ts + kWaves * TT);
+    }
+    issue_fence();
+
+    const SeqRange rg = seq_range_of(p, raw_len);
     const int L = rg.L;
     const int t0 = rg.base + part * p.tokens_per_part;
     const bool direct = p.num_partitions == 1;
@@ -116,18 +144,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     if (!ALIGNED) stage_table_slice(p, b, lb0, lb1, tbl);
     const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
     const int tlb0 = ALIGNED ? 0 : lb0;
-
-    // Q^T as the B operand: head c16 of the group (zero rows past G),
-    // elements 32s + 8*q4 .. +8 for k-step s
-    uint4 qb[KS];
-    {
-        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                               ((int64_t)b * p.num_q_heads + g * G + c16) * D + 8 * q4;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qb[s] = (c16 < G) ? *reinterpret_cast<const uint4*>(qrow + 32 * s)
-                              : make_uint4(0, 0, 0, 0);
-    }
     if (!ALIGNED) __syncthreads();  // publish the staged table slice
 
     const char* kc = static_cast<const char*>(p.k_cache);
@@ -144,12 +160,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // where they measured faster (see launch_one).
     static_assert(ALIGNED || !BUF, "buffer loads need the aligned path");
     constexpr bool kBuf = BUF;
-    auto load_tile = [&](int jj, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
+    auto tile_start = [&](int jj) { return t0 + (kBuf ? jj : min(jj, ntiles - 1)) * TT; };
+    if constexpr (ALIGNED) {
+        // the speculative entries hold for the tiles the wave will load
+        // unless a sliding window moved the partition, or (without buffer
+        // loads) the second tile is past the end and re-reads the last one
+        if (rg.base != 0) first[0] = tile_block(p, trow, tile_start(wave));
+        if (rg.base != 0 || (!kBuf && wave + kWaves >= ntiles))
+            first[1] = tile_block(p, trow, tile_start(wave + kWaves));
+    }
+    // `tb` is the tile's block on the aligned path (tile_block of tile_start)
+    auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
         const bool valid = jj < ntiles;
-        const int tile_base = t0 + min(jj, ntiles - 1) * TT;
-        int phys, slot0, dt;
-        locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, mfma_k_offset(lane), phys, slot0,
-                            dt);
+        const int tile_base = tile_start(jj);
+        int phys = tb.phys, slot0 = tb.slot0, dt;
+        if constexpr (ALIGNED) {
+            dt = tile_row(tile_base, rg.lo, t1, mfma_k_offset(lane));
+        } else {
+            locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, mfma_k_offset(lane), phys, slot0,
+                              dt);
+        }
         {
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + k_lane;
@@ -160,8 +190,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, mfma_v_offset(lane, r), phys,
-                                slot0, dt);
+            if constexpr (ALIGNED) {
+                dt = tile_row(tile_base, rg.lo, t1, mfma_v_offset(lane, r));
+            } else {
+                locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, mfma_v_offset(lane, r), phys,
+                                  slot0, dt);
+            }
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + v_lane;
 #pragma unroll
@@ -169,6 +203,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 vr[r][dh] = kBuf ? load_row16_buf(vc + base, off + 256 * dh, valid)
                                  : load_row16(vc + base + off + 256 * dh);
         }
+    };
+    auto block_of = [&](int jj) {
+        return ALIGNED ? tile_block(p, trow, tile_start(jj)) : TileBlock{0, 0};
     };
 
     // NG = 0: oacc[0][dh][e][r] = O[head 4*q4 + r][d = dh*128 + 8*c16 + e]
@@ -289,14 +326,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     int j = wave;
     uint4 ka[KS], va[4][DH], kb[KS], vb[4][DH];
     if (j < ntiles) {
-        load_tile(j, ka, va);
-        load_tile(j + kWaves, kb, vb);
+        load_tile(j, first[0], ka, va);
+        load_tile(j + kWaves, first[1], kb, vb);
     }
     for (; j < ntiles; j += 2 * kWaves) {
         process(j, ka, va);
-        load_tile(j + 2 * kWaves, ka, va);
+        load_tile(j + 2 * kWaves, block_of(j + 2 * kWaves), ka, va);
         if (j + kWaves < ntiles) process(j + kWaves, kb, vb);
-        load_tile(j + 3 * kWaves, kb, vb);
+        load_tile(j + 3 * kWaves, block_of(j + 3 * kWaves), kb, vb);
     }
 
     // full denominator of head c16 (all four lane groups hold the same m)

@@ -56,7 +56,39 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int c = lane % LPT, r = lane / LPT;
     const int G = p.group;
-    const SeqRange rg = seq_range(p, b);
+    constexpr int S = PDA_VALU_STAGES;
+    static_assert(S >= 2 && S <= 8, "stages");
+
+    // Loads that do not depend on the context length leave together with the
+    // seq_lens load, so the first K/V loads wait for one round trip, not
+    // three: the packed query rows of this KV group (8 elements per lane and
+    // head; padding heads past G read head G-1 again, and their results are
+    // never written), and on the aligned path the table entries of the
+    // wave's first S-1 tiles at the partition's start without a sliding
+    // window.
+    const int raw_len = p.seq_lens[b];
+    uint4 qv[GP];
+    {
+        const uint16_t* qb = static_cast<const uint16_t*>(p.q) +
+                             ((int64_t)b * p.num_q_heads + g * G) * D + c * 8;
+#pragma unroll
+        for (int i = 0; i < GP; ++i)
+            qv[i] = *reinterpret_cast<const uint4*>(qb + (int64_t)min(i, G - 1) * D);
+    }
+    const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+    static_assert(S == 3, "the first-tile table entries are kept for S - 1 = 2 tiles");
+    TileBlock first[S - 1] = {{0, 0}, {0, 0}};
+    if constexpr (ALIGNED) {
+        const int ts = part * p.tokens_per_part + wave * TT;
+        const int lb0 = tile_table_index(p, ts), lb1 = tile_table_index(p, ts + kWaves * TT);
+        const int e0 = table_entry(trow, lb0), e1 = table_entry(trow, lb1);
+        keep_issued(raw_len, e0, e1);
+        first[0] = tile_block_of(p, e0, lb0, ts);
+        first[1] = tile_block_of(p, e1, lb1, ts + kWaves * TT);
+    }
+    issue_fence();
+
+    const SeqRange rg = seq_range_of(p, raw_len);
     const int L = rg.L;
     const int t0 = rg.base + part * p.tokens_per_part;
     const bool direct = p.num_partitions == 1;
@@ -71,17 +103,6 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     if (!ALIGNED) stage_table_slice(p, b, lb0, lb1, tbl);
     const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
     const int tlb0 = ALIGNED ? 0 : lb0;
-
-    // the packed query rows of this KV group: 8 elements per lane and head
-    uint4 qv[GP];
-    {
-        const uint16_t* qb = static_cast<const uint16_t*>(p.q) +
-                             ((int64_t)b * p.num_q_heads + g * G) * D + c * 8;
-#pragma unroll
-        for (int i = 0; i < GP; ++i)
-            qv[i] = (i < G) ? *reinterpret_cast<const uint4*>(qb + (int64_t)i * D)
-                            : make_uint4(0, 0, 0, 0);
-    }
     if (!ALIGNED) __syncthreads();  // publish the staged table slice
 
     const char* kc = static_cast<const char*>(p.k_cache);
@@ -100,13 +121,27 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // measured faster, a group of one head (with more heads the compiler's
     // schedule of the buffer form loses ~1%).
     constexpr bool kBuf = ALIGNED && GP == 1;
-    auto load_tile = [&](int jj, uint4 (&kr)[U], uint4 (&vr)[U]) {
+    auto tile_start = [&](int jj) { return t0 + (kBuf ? jj : min(jj, ntiles - 1)) * TT; };
+    if constexpr (ALIGNED) {
+        // the speculative entries hold for the tiles the wave will load
+        // unless a sliding window moved the partition, or (without buffer
+        // loads) a tile is past the end and re-reads the last one
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st)
+            if (rg.base != 0 || (!kBuf && wave + st * kWaves >= ntiles))
+                first[st] = tile_block(p, trow, tile_start(wave + st * kWaves));
+    }
+    // `tb` is the tile's block on the aligned path (tile_block of tile_start)
+    auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[U], uint4 (&vr)[U]) {
         const bool valid = jj < ntiles;
-        const int tile_base = t0 + min(jj, ntiles - 1) * TT;
+        const int tile_base = tile_start(jj);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int phys, slot0, dt;
-            locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0, dt);
+            int phys = tb.phys, slot0 = tb.slot0, dt;
+            if constexpr (ALIGNED)
+                dt = tile_row(tile_base, rg.lo, t1, u * R + r);
+            else
+                locate_token<R, false>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0, dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + lane_off;
             if constexpr (kBuf) {
@@ -117,6 +152,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
                 vr[u] = load_row16(vc + base + off);
             }
         }
+    };
+    auto block_of = [&](int jj) {
+        return ALIGNED ? tile_block(p, trow, tile_start(jj)) : TileBlock{0, 0};
     };
 
     float m[GP], l[GP], acc[GP][8];
@@ -193,13 +231,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // Register buffers in rotation: while one tile is processed the wave's
     // next tile(s) are already in flight, and no buffer is ever copied (a copy
     // would force a wait for the in-flight loads).
-    constexpr int S = PDA_VALU_STAGES;
-    static_assert(S >= 2 && S <= 8, "stages");
     uint4 kbuf[S][U], vbuf[S][U];
     int j = wave;
     if (j < ntiles) {
 #pragma unroll
-        for (int st = 0; st < S - 1; ++st) load_tile(j + st * kWaves, kbuf[st], vbuf[st]);
+        for (int st = 0; st < S - 1; ++st) load_tile(j + st * kWaves, first[st], kbuf[st], vbuf[st]);
     }
     // Each step refills the buffer freed S-1 steps ago and then processes the
     // oldest one, so S-1 tiles are in flight while one is processed.  One
@@ -208,7 +244,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     for (; j < ntiles; j += S * kWaves) {
 #pragma unroll
         for (int st = 0; st < S; ++st) {
-            load_tile(j + (st + S - 1) * kWaves, kbuf[(st + S - 1) % S], vbuf[(st + S - 1) % S]);
+            const int jn = j + (st + S - 1) * kWaves;
+            load_tile(jn, block_of(jn), kbuf[(st + S - 1) % S], vbuf[(st + S - 1) % S]);
             if (j + st * kWaves < ntiles) process(j + st * kWaves, kbuf[st], vbuf[st]);
         }
     }

@@ -182,15 +182,33 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
 // Tokens of sequence b the decode attends to: [lo, L), lo = max(0, L - W)
 // for a sliding window W > 0, else 0.  The partitions tile [base, L) with
 // base = lo rounded down to the 16-token grid, so that aligned tiles keep
-// starting on it; rows in [base, lo) are redirected to lo (locate_row) and
+// starting on it; rows in [base, lo) are redirected to lo (tile_row) and
 // their scores are masked, so no slot before the window is ever read.
+// seq_range_of takes the raw seq_lens entry, loaded by the caller.
 struct SeqRange {
     int L, lo, base;
 };
-__device__ inline SeqRange seq_range(const DecodeParams& p, int b) {
-    const int L = context_len(p, b);
+__device__ inline SeqRange seq_range_of(const DecodeParams& p, int raw_len) {
+    const int L = max(0, min(raw_len, p.max_seq_len));
     const int lo = p.window > 0 ? max(0, L - p.window) : 0;
     return SeqRange{L, lo, lo & ~(kAlignTokens - 1)};
+}
+__device__ inline SeqRange seq_range(const DecodeParams& p, int b) {
+    return seq_range_of(p, p.seq_lens[b]);
+}
+
+// A compiler barrier for memory operations, emitting no instruction and no
+// wait: the loads issued before it stay before it.  The decode kernels issue
+// their context-independent loads (query rows, first table entries) ahead of
+// the branch on the context length with it; left alone, the compiler sinks
+// them past that branch, behind the seq_lens round trip.
+__device__ inline void issue_fence() { asm volatile("" ::: "memory"); }
+// The same for scalar loads of constant memory (table entries), which the
+// fence does not hold: a use in place keeps them, together with the seq_lens
+// load.  It waits for the three values, as the context-length branch after
+// it would wait for seq_lens alone: the scalar loads are in flight together.
+__device__ inline void keep_issued(int len, int e0, int e1) {
+    asm volatile("" ::"s"(len), "s"(e0), "s"(e1));
 }
 
 // Partitions of a unit that hold tokens (the rest are empty).
@@ -198,37 +216,62 @@ __device__ inline int live_partitions(const DecodeParams& p, const SeqRange& r) 
     return min(p.num_partitions, (r.L - r.base + p.tokens_per_part - 1) / p.tokens_per_part);
 }
 
-// Physical block and slot of the row a lane reads: the token at in-tile
-// offset `o` of the tile starting at tile_base, slot = slot0 + dt.  Tokens at
-// or past t1 (the partition end, never past the sequence end) are redirected
-// to token t1-1, and tokens before lo (the first token attended to) to lo,
-// so no slot past seq_len or before a sliding window is ever addressed.  Block ids
-// are clamped into the pool, so a corrupt table entry gives a wrong row,
-// never an access outside the pool.
-//  ALIGNED (block size a multiple of 16, tiles starting at multiples of 16
-//  tokens or of the round length): all offsets a wave reads together lie in
-//  the 16-token group that contains offset o0 (wave-uniform), which lies in
-//  one block; phys and slot0 are located once from o0 and are wave-uniform,
-//  dt is the lane's row offset.  `tbl` is then the sequence's block-table row
-//  in global memory (lb0 = 0), read with a scalar load at the wave-uniform
-//  index: no staging, no barrier, and no vector register is taken.
+// The block of the aligned path's tile that starts at tile_base (a multiple
+// of 16 tokens or of the round length, with the block size a multiple of 16):
+// every row a wave reads with that tile lies in the tile's 16-token group,
+// hence in this block.  `row` is the sequence's block-table row in global
+// memory, read with a scalar load (wave-uniform index: no staging, no barrier,
+// no vector register).  The index does not depend on the context length, so
+// the first tiles' entries can be loaded while the length is still in flight;
+// it is clamped into the row, so a tile past the end (a prefetch that loads
+// nothing) reads an entry inside the row.  Block ids are clamped into the
+// pool, so a corrupt entry gives a wrong row, never an access outside the
+// pool.
+struct TileBlock {
+    int phys, slot0;
+};
+__device__ inline int tile_table_index(const DecodeParams& p, int tile_base) {
+    return min((int)fastdiv((uint32_t)tile_base, p.bs_div), p.max_blocks_per_seq - 1);
+}
+__device__ inline int table_entry(const int32_t* row, int lb) {
+    typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+    return ((const_i32p)row)[lb];  // address-space cast: C-style only
+}
+__device__ inline TileBlock tile_block_of(const DecodeParams& p, int entry, int lb, int tile_base) {
+    return TileBlock{min(max(entry, 0), p.num_blocks - 1), tile_base - lb * p.block_size};
+}
+__device__ inline TileBlock tile_block(const DecodeParams& p, const int32_t* row, int tile_base) {
+    const int lb = tile_table_index(p, tile_base);
+    return tile_block_of(p, table_entry(row, lb), lb, tile_base);
+}
+
+// In-tile offset of the row a lane reads for in-tile offset o: tokens at or
+// past t1 (the partition end, never past the sequence end) are redirected to
+// token t1-1, and tokens before lo (the first token attended to) to lo, so no
+// slot past seq_len or before a sliding window is ever addressed.
+__device__ inline int tile_row(int tile_base, int lo, int t1, int o) {
+    return min(max(o, lo - tile_base), t1 - 1 - tile_base);
+}
+
+// Physical block and slot of the row a lane reads, slot = slot0 + dt (rows
+// redirected as in tile_row).
+//  ALIGNED: phys and slot0 are those of the tile (tile_block), wave-uniform;
+//  dt is the lane's row offset.  `tbl` is the sequence's block-table row in
+//  global memory (lb0 = 0).
 //  Otherwise `tbl` is the LDS copy of the slice starting at block lb0, every
 //  lane divides its own token index by the block size and dt = 0.
 template <bool ALIGNED>
 __device__ inline void locate_row(const DecodeParams& p, const int32_t* tbl, int lb0,
-                                  int tile_base, int lo, int t1, int o0, int o, int& phys,
-                                  int& slot0, int& dt) {
-    const int first = lo - tile_base, last = t1 - 1 - tile_base;
-    const int t = tile_base + min(max(o, first), last);
+                                  int tile_base, int lo, int t1, int o, int& phys, int& slot0,
+                                  int& dt) {
+    const int ot = tile_row(tile_base, lo, t1, o);
     if constexpr (ALIGNED) {
-        const int ub = tile_base + min(max(o0, first), last);
-        const int lb = (int)fastdiv((uint32_t)ub, p.bs_div);
-        slot0 = ub - lb * p.block_size;
-        dt = t - ub;
-        typedef const __attribute__((address_space(4))) int32_t* const_i32p;
-        phys = ((const_i32p)tbl)[lb - lb0];  // address-space cast: C-style only
-        phys = min(max(phys, 0), p.num_blocks - 1);
+        const TileBlock tb = tile_block(p, tbl, tile_base);
+        phys = tb.phys;
+        slot0 = tb.slot0;
+        dt = ot;
     } else {
+        const int t = tile_base + ot;
         const int lb = (int)fastdiv((uint32_t)t, p.bs_div);
         slot0 = t - lb * p.block_size;
         dt = 0;
@@ -242,7 +285,7 @@ template <int R, bool ALIGNED>
 __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, int lb0,
                                     int tile_base, int lo, int t1, int u, int r, int& phys,
                                     int& slot0, int& dt) {
-    locate_row<ALIGNED>(p, tbl, lb0, tile_base, lo, t1, u * R, u * R + r, phys, slot0, dt);
+    locate_row<ALIGNED>(p, tbl, lb0, tile_base, lo, t1, u * R + r, phys, slot0, dt);
 }
 
 // ---- MFMA tile geometry --------------------------------------------------

@@ -59,14 +59,14 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
             }
         } else if constexpr (ROWS == 1) {
             const int o = mfma_k_offset(lane);
-            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, o, phys, slot0, dt);
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, o, phys, slot0, dt);
             const int t = tile_base + o;
             if ((lane >> 4) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int o = mfma_v_offset(lane, rr);
-                locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, 0, o, phys, slot0, dt);
+                locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, o, phys, slot0, dt);
                 const int t = tile_base + o;
                 if ((lane & 15) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
