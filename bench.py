@@ -296,6 +296,9 @@ def main():
         specs += [("cfg5 B64 mixed", lambda: configs.cfg5(device="cuda"))]
         specs += [(f"cfg3 sliding W1024 B{b} 32K", lambda b=b: configs.cfg3_sliding(b, L, device="cuda"))
                   for b in (1, 8)]
+        specs += [("cfg4 TP2 share 12/2 32K", lambda: configs.cfg4_tp2(L, device="cuda"))]
+        specs += [(f"cfg3 TP2 share 16/8 B{b} 32K", lambda b=b: configs.cfg3_tp2(b, L, device="cuda"))
+                  for b in (1, 8)]
         for name, mk in specs:
             log(f"timing {name}")
             c = mk()

@@ -17,6 +17,10 @@
   cfg5  batched mixed-length decode: B 64, Hq 32 / Hkv 8, D 128, bs 16,
         L_b ~ U[1K, 32K] redrawn while a multiple of 16, fragmented tables over
         one shared pool, NaN tails.
+  TP shares: one GPU's half of cfg4 (Hq 12 / Hkv 2) and of cfg3 (Hq 16 / Hkv 8)
+        when the heads are split over two GPUs (the pages run the model at
+        TP=2: page "vLLM's custom ROCm paged-attention kernel wins all sixty
+        cells", section 4); same shapes otherwise.
 Lengths "1K..32K" are read as powers of two, 1024..32768; "16k+1" and "16k+7"
 as 16385 and 16391.
 """
@@ -58,6 +62,19 @@ def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu
 def cfg4(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:
     return make_case(B=1, Hq=24, Hkv=4, D=256, bs=784, seq_lens=[L], dtype=dtype,
                      seed=seed_for(4, cell), device=device, extra_blocks=1,
+                     tail_k=tail, tail_v=tail)
+
+
+def cfg4_tp2(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:
+    return make_case(B=1, Hq=12, Hkv=2, D=256, bs=784, seq_lens=[L], dtype=dtype,
+                     seed=seed_for(4, 200 + cell), device=device, extra_blocks=1,
+                     tail_k=tail, tail_v=tail)
+
+
+def cfg3_tp2(B: int, L: int, dtype: str = "bf16", device="cpu", tail: str = "nan",
+             cell: int = 0) -> Case:
+    return make_case(B=B, Hq=16, Hkv=8, D=128, bs=16, seq_lens=[L] * B, dtype=dtype,
+                     seed=seed_for(3, 200 + cell), device=device, extra_blocks=1,
                      tail_k=tail, tail_v=tail)
 
 

@@ -325,3 +325,20 @@ def test_bookkeeping_trace_cfg5_full_size(variant, rows):
     assert np.array_equal(part[valid], e_part[valid])
     assert np.all(slot[~valid] == -1)
     assert np.array_equal(ranges.cpu().numpy(), e_ranges)
+
+
+# ---- one GPU's share of the heads under two-way tensor parallelism -------
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+@pytest.mark.parametrize("L", [500, 4096, 16391, 32768])
+def test_tp_share_cfg4_12_2(L, variant):
+    case = configs.cfg4_tp2(L, device="cuda")
+    check(case, run(case, plan=device_plan(case, variant)), per_seq=True)
+
+
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+@pytest.mark.parametrize("B,L", [(1, 1024), (1, 16391), (1, 32768), (8, 4090), (8, 32768)])
+def test_tp_share_cfg3_16_8(B, L, variant):
+    case = configs.cfg3_tp2(B, L, device="cuda")
+    got = run(case, plan=device_plan(case, variant))
+    seqs = None if B == 1 else [0, 5, 7]
+    check(case, got, seqs=seqs, per_seq=True)
