@@ -42,6 +42,18 @@
  * partitions then tile [base, L) with base = max(0, L - W) rounded down to a
  * multiple of 16, and the plan is sized for that span (see below).
  *
+ * Multi-row decode (pda_shape_t.q_len = n > 1): each sequence brings n new
+ * query rows at once -- the speculative or multi-token decode whose extra
+ * rows the pages ask about (first page, section 6, "One machine, and the
+ * model runner question") -- whose K and V are already in the cache as its
+ * last n tokens.  Row i (0 <= i < n) sits at position L - n + i and attends
+ * causally, to t in [lo_i, e_i) with e_i = L - n + i + 1 and lo_i = 0, or
+ * max(0, e_i - W) with a sliding window; row n-1 is the plain decode over
+ * the whole context.  q and out are then [B][n][Hq][D]; a unit (b, g) packs
+ * R = n * G rows (row r = query position r / G, head r % G of the group), and
+ * the kernels read every K/V byte once for all R rows.  A row whose range is
+ * empty (L < n) yields zeros.
+ *
  * Device-data contract (not checked on the hot path; violating it is
  * undefined behaviour):
  *  - 0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size;
@@ -74,30 +86,35 @@ extern "C" {
 #define PDA_BF16 0
 #define PDA_FP16 1
 
-/* Largest supported query-to-KV head ratio G. */
+/* Largest supported query-to-KV head ratio G, and largest number of rows
+ * R = q_len * G one unit packs (two 16-row matrix-core tiles). */
 #define PDA_MAX_GROUP 16
+#define PDA_MAX_ROWS  32
 
 /* ---- kernel variants --------------------------------------------------- */
 /* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
  *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
  * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs, the
- *   packed query group padded to 16 rows) and PV with fp32 weights and exact
- *   fp32 V, on v_mfma_f32_4x4x1_16b_f32 blocks of 4 heads for G <= 4 (and
- *   G <= 8 at head sizes up to 128), else on v_mfma_f32_16x16x4_f32 with the
- *   group padded to 16; G <= PDA_MAX_GROUP. */
+ *   packed rows padded to 16 per tile) and PV with fp32 weights and exact
+ *   fp32 V, on v_mfma_f32_4x4x1_16b_f32 blocks of 4 rows for R <= 4 (and
+ *   R <= 8 at head sizes up to 128), else on v_mfma_f32_16x16x4_f32 with the
+ *   rows padded to 16 per tile; R <= PDA_MAX_ROWS.
+ * R = q_len * G is the number of rows a unit packs (G for plain decode);
+ * the VALU variant serves R <= PDA_VALU_MAX_GROUP. */
 #define PDA_VARIANT_VALU 1
 #define PDA_VARIANT_MFMA 2
 #define PDA_VALU_MAX_GROUP 8
 
 /* ---- the plan -------------------------------------------------------------
- * A pure integer function of (num_seqs B, num_kv_heads Hkv, G = Hq/Hkv,
- * head_size D, span Lmax, compute-unit count C), where the span is
- * max_seq_len, or min(max_seq_len, W + 15) with a sliding window W > 0 (the
- * window rounded out to the 16-token grid the partitions start on):
+ * A pure integer function of (num_seqs B, num_kv_heads Hkv, rows per unit
+ * R = q_len * G, head_size D, span Lmax, compute-unit count C), where the
+ * span is max_seq_len, or min(max_seq_len, W + q_len - 1 + 15) with a
+ * sliding window W > 0 (the union of the rows' windows, rounded out to the
+ * 16-token grid the partitions start on):
  *
- * Variant: MFMA if G > PDA_VALU_MAX_GROUP, or if G >= PDA_MFMA_MIN_GROUP and
+ * Variant: MFMA if R > PDA_VALU_MAX_GROUP, or if R >= PDA_MFMA_MIN_GROUP and
  *   B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU load of the matrix cores
- *   pays); VALU otherwise (one head per group, where the VALU kernel has
+ *   pays); VALU otherwise (one row per unit, where the VALU kernel has
  *   the least to do, or many units over many rounds, where its higher
  *   occupancy pays).
  * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D (K and V bytes per
@@ -117,7 +134,9 @@ extern "C" {
  *   a workgroup's start-up and epilogue again and doubles the partials the
  *   merge reads; one workgroup per CU measured fastest for both variants.)
  * Partition p of (b, g) covers tokens [base + p*T_p, min(base + (p+1)*T_p,
- * seq_lens[b])), base = 0 without a window; it is empty when that range is.  The grid of the main kernel is
+ * seq_lens[b])), base = 0 without a window, else lo_0 (the first row's
+ * window start) rounded down to a multiple of 16; it is empty when that
+ * range is.  The grid of the main kernel is
  * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
  * workspace is used; otherwise it writes fp32 partials that are merged with
  * the log-sum-exp rule, either
@@ -128,8 +147,8 @@ extern "C" {
  *                    with an atomic counter in the workspace (one launch;
  *                    that workgroup alone reads P x G x D partials, which
  *                    only pays when that product is small).
- * The workspace holds partial outputs [B][Hq][P][D] fp32, then (m, l) pairs
- * [B][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
+ * The workspace holds partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
+ * pairs [B][q_len][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
  * aligned to 256 bytes.  The counters must be zero when a fused call starts;
  * every fused call leaves them zero again, so a workspace needs zeroing once
  * (paged_decode_attn_workspace_init, or any zero fill) before its first use.
@@ -155,7 +174,8 @@ typedef struct pda_shape {
     int32_t max_blocks_per_seq;  /* MBS >= 1: row length of block_table */
     int32_t max_seq_len;         /* >= every seq_lens[b], <= MBS * bs; sizes the plan */
     int32_t dtype;               /* PDA_BF16 or PDA_FP16 */
-    int32_t sliding_window;      /* W >= 0; 0: attend to the whole context (see below) */
+    int32_t sliding_window;      /* W >= 0; 0: attend to the whole context (see above) */
+    int32_t q_len;               /* query rows per sequence, 1..; 0 is read as 1 (see above) */
 } pda_shape_t;
 
 typedef struct pda_plan {
@@ -191,13 +211,13 @@ int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
 int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream);
 
 /* The decode step, under the device's own plan.
- *   q            [B][Hq][D]           16-bit, the one query token per sequence
+ *   q            [B][q_len][Hq][D]    16-bit, the query rows of each sequence
  *   k_cache      [NB][Hkv][bs][D]     16-bit, the paged K pool
  *   v_cache      [NB][Hkv][bs][D]     16-bit, the paged V pool (same layout)
  *   block_table  [B][MBS]             int32 physical block ids, row-major
  *   seq_lens     [B]                  int32 context lengths
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(D))
- *   out          [B][Hq][D]           16-bit, written in full
+ *   out          [B][q_len][Hq][D]    16-bit, written in full
  *   workspace    device scratch of workspace_bytes (may be NULL if the plan
  *                needs none), zeroed once before its first use (see above)
  * Returns PDA_OK once the kernels are enqueued on `stream`. */

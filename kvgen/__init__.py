@@ -51,7 +51,7 @@ class Case:
     bs: int
     dtype: str
     seq_lens: List[int]
-    q: torch.Tensor                 # [B, Hq, D] 16-bit
+    q: torch.Tensor                 # [B, Hq, D] 16-bit ([B, q_len, Hq, D] for q_len > 1)
     k: List[torch.Tensor]           # per b: [Hkv, L_b, D] 16-bit, pre-paging
     v: List[torch.Tensor]
     k_cache: torch.Tensor           # [NB, Hkv, bs, D] 16-bit
@@ -66,15 +66,19 @@ class Case:
     tail_k: str = "zero"
     tail_v: str = "zero"
     sliding_window: int = 0         # W > 0: decode attends to the last W tokens
+    q_len: int = 1                  # query rows per sequence (causal among themselves)
 
     @property
     def G(self) -> int:
         return self.Hq // self.Hkv
 
     def attended(self, b: int) -> int:
-        """Tokens of sequence b the decode attends to."""
+        """Tokens of sequence b the decode reads: the union of its rows'
+        ranges (the last W + q_len - 1 tokens with a sliding window W)."""
         L = self.seq_lens[b]
-        return min(L, self.sliding_window) if self.sliding_window > 0 else L
+        if self.sliding_window > 0:
+            return min(L, self.sliding_window + self.q_len - 1)
+        return L
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes: attended tokens only, K and V, 16-bit."""
@@ -85,14 +89,16 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
               dtype: str = "bf16", seed: int = 0, device="cpu", extra_blocks: int = 1,
               max_blocks_per_seq: Optional[int] = None, tail_k: str = "zero",
               tail_v: str = "zero", scale: Optional[float] = None,
-              max_seq_len: Optional[int] = None, sliding_window: int = 0) -> Case:
+              max_seq_len: Optional[int] = None, sliding_window: int = 0,
+              q_len: int = 1) -> Case:
     assert len(seq_lens) == B and Hq % Hkv == 0
     tdt = _DT[dtype]
     device = torch.device(device)
     gen = torch.Generator(device=device)
     gen.manual_seed(int(seed))
     lens = [int(x) for x in seq_lens]
-    q = torch.randn((B, Hq, D), generator=gen, device=device).to(tdt)
+    qshape = (B, Hq, D) if q_len == 1 else (B, q_len, Hq, D)
+    q = torch.randn(qshape, generator=gen, device=device).to(tdt)
     k, v = [], []
     for b in range(B):
         k.append(torch.randn((Hkv, lens[b], D), generator=gen, device=device).to(tdt))
@@ -116,7 +122,7 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
                 num_blocks=NB, max_blocks_per_seq=MBS,
                 max_seq_len=int(max_seq_len) if max_seq_len is not None else max(lens),
                 unref_ids=unref, tail_k=tail_k, tail_v=tail_v,
-                sliding_window=int(sliding_window))
+                sliding_window=int(sliding_window), q_len=int(q_len))
     return page(case, tail_k=tail_k, tail_v=tail_v)
 
 
@@ -167,13 +173,13 @@ def repermute(case: Case, seed: int) -> Case:
 
 def poison_before_window(case: Case, fill: str = "nan") -> Case:
     """The same case with the cache slots of every token before its sequence's
-    sliding window (t < L_b - W) overwritten with `fill`: tokens the decode
-    must not read."""
+    sliding window (t < L_b - q_len + 1 - W, before the window of its earliest
+    query row) overwritten with `fill`: tokens the decode must not read."""
     assert case.sliding_window > 0
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
     table = case.block_table.cpu().to(torch.int64)
     for b in range(case.B):
-        lo = max(0, case.seq_lens[b] - case.sliding_window)
+        lo = max(0, case.seq_lens[b] - case.q_len + 1 - case.sliding_window)
         if lo == 0:
             continue
         t = torch.arange(lo)
@@ -200,4 +206,4 @@ def shape_dict(case: Case) -> dict:
     return dict(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
                 head_size=case.D, block_size=case.bs, num_blocks=case.num_blocks,
                 max_blocks_per_seq=case.max_blocks_per_seq, max_seq_len=case.max_seq_len,
-                dtype=case.dtype, sliding_window=case.sliding_window)
+                dtype=case.dtype, sliding_window=case.sliding_window, q_len=case.q_len)

@@ -21,6 +21,8 @@
         when the heads are split over two GPUs (the pages run the model at
         TP=2: page "vLLM's custom ROCm paged-attention kernel wins all sixty
         cells", section 4); same shapes otherwise.
+Every shape takes q_len > 1 for multi-row decode (that many query rows at
+the end of each sequence, causal among themselves).
 Lengths "1K..32K" are read as powers of two, 1024..32768; "16k+1" and "16k+7"
 as 16385 and 16391.
 """
@@ -40,16 +42,17 @@ def cfg1(dtype: str = "bf16", device="cpu", tail: str = "nan") -> Case:
                      tail_k=tail, tail_v=tail)
 
 
-def cfg2(hq: int, L: int, device="cpu", dtype: str = "bf16", cell: int = 0) -> Case:
+def cfg2(hq: int, L: int, device="cpu", dtype: str = "bf16", cell: int = 0,
+         q_len: int = 1) -> Case:
     return make_case(B=1, Hq=hq, Hkv=8, D=128, bs=16, seq_lens=[L], dtype=dtype,
-                     seed=seed_for(2, cell), device=device, extra_blocks=1)
+                     seed=seed_for(2, cell), device=device, extra_blocks=1, q_len=q_len)
 
 
 def cfg3(B: int, L: int, dtype: str = "bf16", device="cpu", tail_k: str = "nan",
-         tail_v: str = "nan", cell: int = 0) -> Case:
+         tail_v: str = "nan", cell: int = 0, q_len: int = 1) -> Case:
     return make_case(B=B, Hq=32, Hkv=16, D=128, bs=16, seq_lens=[L] * B, dtype=dtype,
                      seed=seed_for(3, cell), device=device, extra_blocks=1,
-                     tail_k=tail_k, tail_v=tail_v)
+                     tail_k=tail_k, tail_v=tail_v, q_len=q_len)
 
 
 def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu",
@@ -59,10 +62,11 @@ def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu
                      tail_k=tail, tail_v=tail, sliding_window=W)
 
 
-def cfg4(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:
+def cfg4(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0,
+         q_len: int = 1) -> Case:
     return make_case(B=1, Hq=24, Hkv=4, D=256, bs=784, seq_lens=[L], dtype=dtype,
                      seed=seed_for(4, cell), device=device, extra_blocks=1,
-                     tail_k=tail, tail_v=tail)
+                     tail_k=tail, tail_v=tail, q_len=q_len)
 
 
 def cfg4_tp2(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:
@@ -90,8 +94,8 @@ def cfg5_lens(seed: int, B: int = 64, lo: int = 1024, hi: int = 32768):
 
 
 def cfg5(device="cpu", dtype: str = "bf16", B: int = 64, lo: int = 1024, hi: int = 32768,
-         cell: int = 0) -> Case:
+         cell: int = 0, q_len: int = 1) -> Case:
     seed = seed_for(5, cell)
     lens = cfg5_lens(seed + 1, B=B, lo=lo, hi=hi)
     return make_case(B=B, Hq=32, Hkv=8, D=128, bs=16, seq_lens=lens, dtype=dtype, seed=seed,
-                     device=device, extra_blocks=1, tail_k="nan", tail_v="nan")
+                     device=device, extra_blocks=1, tail_k="nan", tail_v="nan", q_len=q_len)

@@ -14,6 +14,15 @@ Contents
                                    reference at fp32 computed from pre-paging
                                    KV (page "vLLM's custom ROCm paged-attention
                                    kernel wins all sixty cells", section 1).
+  decode_multi                     multi-row decode: q_len query rows per
+                                   sequence at its last q_len positions, row
+                                   i attending causally to the prefix that
+                                   ends at its own position -- each row is
+                                   plain decode over that prefix (the
+                                   speculative / multi-token decode the
+                                   pages ask about: first page, section 6,
+                                   "One machine, and the model runner
+                                   question").
   plan                             the partition plan, re-derived from its
                                    documentation in include/pda.h (plan.py).
   bookkeeping                      expected per-token physical slot and
@@ -126,6 +135,27 @@ def decode(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.n
     if rc != 0:
         raise ValueError("oracle_decode failed")
     return out
+
+
+def decode_multi(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.ndarray:
+    """q float32 [B, n, Hq, D]: n query rows per sequence, row i at position
+    L - n + i.  Row i attends to the tokens t <= L - n + i (causal among the
+    new rows, whose K/V are the sequence's last n), and with a sliding window
+    W > 0 to the last W of those.  So row i is the plain decode of the
+    sequence truncated to its first L - n + i + 1 tokens (zeros when that is
+    not positive).  Returns float32 [B, n, Hq, D]."""
+    q = np.asarray(q, dtype=np.float32)
+    B, n, Hq, D = q.shape
+    kk, vv, ll = [], [], []
+    for b in range(B):
+        L = int(seq_lens[b])
+        for i in range(n):
+            e = max(0, L - n + i + 1)
+            kk.append(np.asarray(k[b])[:, :e])
+            vv.append(np.asarray(v[b])[:, :e])
+            ll.append(e)
+    out = decode(q.reshape(B * n, Hq, D), kk, vv, ll, scale, nthreads=nthreads, window=window)
+    return out.reshape(B, n, Hq, D)
 
 
 def decode_rows(q, k, v, seq_lens, scale, rows, nthreads: int = 0, window: int = 0) -> np.ndarray:

@@ -19,20 +19,22 @@ import numpy as np
 
 def expected_trace(block_table, seq_lens, num_kv_heads: int, block_size: int,
                    max_seq_len: int, num_partitions: int, tokens_per_partition: int,
-                   window: int = 0):
+                   window: int = 0, q_len: int = 1):
     """Returns (slot, part, ranges, valid):
       slot  [B, Hkv, max_seq_len] int64  physical slot block_id*bs + t%bs
       part  [B, Hkv, max_seq_len] int64  partition that owns token t
       ranges [B, Hkv, P, 2] int64        (t0, t1) per unit
       valid [B, Hkv, max_seq_len] bool   t attended to: lo_b <= t < seq_lens[b]
-    With a sliding window W > 0, lo_b = max(0, L_b - W) and the partitions of
-    sequence b tile [base_b, L_b), base_b = lo_b rounded down to a multiple of
-    16; without one, lo_b = base_b = 0.
+    With a sliding window W > 0, lo_b = max(0, L_b - q_len + 1 - W) (the
+    window of the first of the q_len query rows, the earliest one) and the
+    partitions of sequence b tile [base_b, L_b), base_b = lo_b rounded down
+    to a multiple of 16; without one, lo_b = base_b = 0.
     """
     bt = np.asarray(block_table, dtype=np.int64)
     lens = np.asarray(seq_lens, dtype=np.int64)
     B = bt.shape[0]
-    lo = np.maximum(lens - window, 0) if window > 0 else np.zeros_like(lens)
+    n = max(1, q_len)
+    lo = np.maximum(lens - n + 1 - window, 0) if window > 0 else np.zeros_like(lens)
     base = (lo // 16) * 16
     t = np.arange(max_seq_len, dtype=np.int64)
     valid = (t[None, :] < lens[:, None]) & (t[None, :] >= lo[:, None])   # [B, Lmax]

@@ -26,10 +26,12 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def variant(num_seqs: int, num_kv_heads: int, group: int) -> int:
-    """MFMA above the VALU group limit, or for G >= 2 with at most 128 units."""
+def variant(num_seqs: int, num_kv_heads: int, group: int, q_len: int = 1) -> int:
+    """MFMA above the VALU row limit, or for R = q_len * G >= 2 rows with at
+    most 128 units."""
     units = num_seqs * num_kv_heads
-    if group > VALU_MAX_GROUP or (group >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
+    rows = max(1, q_len) * group
+    if rows > VALU_MAX_GROUP or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
         return MFMA
     return VALU
 
@@ -43,21 +45,22 @@ def token_bounds(head_size: int):
     return t_min, t_many, t_one
 
 
-def span(max_seq_len: int, window: int = 0) -> int:
+def span(max_seq_len: int, window: int = 0, q_len: int = 1) -> int:
     """Tokens the partitions must cover: max_seq_len, or with a sliding
-    window W > 0 at most W + 15 (the window, from its first token rounded
-    down to a multiple of 16)."""
-    return min(max_seq_len, window + 15) if window > 0 else max_seq_len
+    window W > 0 at most W + q_len - 1 + 15 (the union of the q_len rows'
+    windows, from its first token rounded down to a multiple of 16)."""
+    n = max(1, q_len)
+    return min(max_seq_len, window + n - 1 + 15) if window > 0 else max_seq_len
 
 
 def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_seq_len: int,
-              cu_count: int, window: int = 0):
+              cu_count: int, window: int = 0, q_len: int = 1):
     """(P, T_p, variant) for the documented rule."""
-    var = variant(num_seqs, num_kv_heads, group)
+    var = variant(num_seqs, num_kv_heads, group, q_len)
     t_min, t_many, t_one = token_bounds(head_size)
     units = num_seqs * num_kv_heads
     p_fill = _cdiv(cu_count, units)
-    lspan = span(max_seq_len, window)
+    lspan = span(max_seq_len, window, q_len)
     if lspan <= 0:
         t_p = t_min
     else:
@@ -68,15 +71,16 @@ def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,
-                    num_kv_heads: int = 1) -> int:
-    """Partial outputs [B][Hq][P][D] fp32, then (m, l) [B][Hq][P][2] fp32,
-    then arrival counters [B][Hkv] int32, each part rounded up to 256 bytes;
-    none when P == 1."""
+                    num_kv_heads: int = 1, q_len: int = 1) -> int:
+    """Partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
+    [B][q_len][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
+    rounded up to 256 bytes; none when P == 1."""
     if p <= 1:
         return 0
 
     def r256(x):
         return _cdiv(x, 256) * 256
-    return (r256(num_seqs * num_q_heads * p * head_size * 4)
-            + r256(num_seqs * num_q_heads * p * 2 * 4)
+    rows = num_seqs * max(1, q_len) * num_q_heads
+    return (r256(rows * p * head_size * 4)
+            + r256(rows * p * 2 * 4)
             + r256(num_seqs * num_kv_heads * 4))

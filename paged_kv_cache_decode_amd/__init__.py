@@ -40,7 +40,8 @@ class PdaShape(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("sliding_window", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("sliding_window", ctypes.c_int32),
+                ("q_len", ctypes.c_int32)]
 
 
 class PdaPlan(ctypes.Structure):
@@ -103,18 +104,27 @@ def load_library():
 
 
 def make_shape(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
-               max_blocks_per_seq, max_seq_len, dtype="bf16", sliding_window=0) -> PdaShape:
-    """sliding_window W > 0: attend to the last W tokens of each sequence."""
+               max_blocks_per_seq, max_seq_len, dtype="bf16", sliding_window=0,
+               q_len=1) -> PdaShape:
+    """sliding_window W > 0: attend to the last W tokens of each sequence.
+    q_len > 1: that many query rows per sequence, causal among themselves."""
     dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
     return PdaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_size),
                     int(block_size), int(num_blocks), int(max_blocks_per_seq), int(max_seq_len),
-                    dt, int(sliding_window))
+                    dt, int(sliding_window), int(q_len))
 
 
 def shape_from_tensors(q, k_cache, block_table, max_seq_len: int,
                        sliding_window: int = 0) -> PdaShape:
+    """q is [B, Hq, D] (one query row per sequence) or [B, q_len, Hq, D]."""
     import torch
-    B, Hq, D = q.shape
+    if q.dim() == 3:
+        B, Hq, D = q.shape
+        q_len = 1
+    elif q.dim() == 4:
+        B, q_len, Hq, D = q.shape
+    else:
+        raise ValueError("q must be [B, Hq, D] or [B, q_len, Hq, D]")
     NB, Hkv, bs, D2 = k_cache.shape
     if D2 != D:
         raise ValueError("head size of q and k_cache differ")
@@ -122,7 +132,7 @@ def shape_from_tensors(q, k_cache, block_table, max_seq_len: int,
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
     return make_shape(B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seq_len, dt,
-                      sliding_window)
+                      sliding_window, q_len)
 
 
 def pda_status_string(status: int) -> str:
@@ -198,9 +208,11 @@ def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
 def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, out=None,
                       workspace=None, max_seq_len: Optional[int] = None, plan: Optional[PdaPlan] = None,
                       stream=None, sliding_window: int = 0):
-    """Decode one query token per sequence over the paged KV cache.
+    """Decode the query rows of each sequence over the paged KV cache.
 
-    q [B, Hq, D], k_cache/v_cache [NB, Hkv, bs, D] (bf16 or fp16, one dtype),
+    q [B, Hq, D] (one row per sequence) or [B, q_len, Hq, D] (q_len rows at
+    the sequence's last q_len positions, causal among themselves),
+    k_cache/v_cache [NB, Hkv, bs, D] (bf16 or fp16, one dtype),
     block_table [B, MBS] int32, seq_lens [B] int32, all on the current device.
     max_seq_len must bound every seq_lens entry (default: block_table width *
     block size, which is always valid but may over-partition).

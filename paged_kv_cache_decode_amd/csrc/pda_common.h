@@ -48,7 +48,7 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, const FastDiv& f) {
 struct DecodeParams {
     // what a decode workgroup needs first (its first table entries and the
     // context length) fills the first 64 bytes, which one scalar load brings
-    const void* q;             // [B][Hq][D]
+    const void* q;             // [B][q_len][Hq][D]
     const int32_t* block_table;// [B][MBS]
     const int32_t* seq_lens;   // [B]
     int32_t tokens_per_part;   // T_p
@@ -58,12 +58,12 @@ struct DecodeParams {
     int32_t num_q_heads;       // Hq
     int32_t max_seq_len;       // host bound on seq_lens (also the trace row length)
     int32_t window;            // sliding window W (0: whole context)
-    int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
+    int32_t q_len;             // query rows per sequence (1: plain decode)
     const void* k_cache;       // [NB][Hkv][bs][D]
     const void* v_cache;       // [NB][Hkv][bs][D]
-    void* out;                 // [B][Hq][D]
-    float* ws_o;               // [B][Hq][P][D]    (P > 1 only)
-    float* ws_ml;              // [B][Hq][P][2]    (P > 1 only)
+    void* out;                 // [B][q_len][Hq][D]
+    float* ws_o;               // [B][q_len][Hq][P][D]    (P > 1 only)
+    float* ws_ml;              // [B][q_len][Hq][P][2]    (P > 1 only)
     int32_t* counters;         // [B][Hkv] arrival counters (fused merge)
     int32_t* trace_slot;       // trace kernel only
     int32_t* trace_part;
@@ -74,10 +74,12 @@ struct DecodeParams {
     int32_t num_partitions;    // P
     int32_t tbl_capacity;      // LDS entries reserved for the block-table slice
     int32_t fused_merge;       // 1: the last unit of each (b, g) merges the partials
+    int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
+    int32_t rows;              // R = q_len * G rows per unit
     int64_t block_stride;      // Hkv * bs * D elements
     int32_t head_stride;       // bs * D elements
 };
-static_assert(offsetof(DecodeParams, num_blocks) + sizeof(int32_t) <= 64,
+static_assert(offsetof(DecodeParams, q_len) + sizeof(int32_t) <= 64,
               "the start-up fields fit one 64-byte scalar load");
 
 constexpr int kWave = 64;

@@ -1,27 +1,29 @@
 // Paged-attention decode, matrix-core variant, for gfx950.
 //
 // Same unit of work as the VALU variant -- one workgroup of 4 wavefronts per
-// (partition p, KV head g, sequence b), all G query heads of the group packed,
-// every K/V byte read once -- but both contractions run on MFMA, with the
-// packed group padded to 16 rows:
+// (partition p, KV head g, sequence b), all rows of the unit packed (the G
+// query heads of the group, for each of the q_len query positions), every
+// K/V byte read once -- but both contractions run on MFMA, with the packed
+// rows padded to 16 per chunk:
 //
 //   QK^T  S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: a 16-token tile of K
 //         rows is the A operand (lane l loads 16 bytes of token l%16), Q^T the
 //         B operand.  The 16x16 result leaves each lane the scores of one
-//         head (l%16) for four tokens (4(l/16) + r, r = 0..3).
-//   mask  scores of tokens at or past the partition end become -inf by select;
-//         tail slots are never addressed (see locate_row).
+//         row (l%16) for four tokens (4(l/16) + r, r = 0..3).
+//   mask  scores of tokens at or past the partition end, outside a sliding
+//         window or after the row's causal end become -inf by select; tail
+//         slots and slots before a window are never addressed (see tile_row).
 //   softmax  online, exp2 domain; the running max per head is shared by the
 //         four lanes that hold that head; the accumulator is rescaled only
 //         when some max grew.
 //   PV    O = P V on v_mfma_f32_16x16x4_f32: the exp'd scores are already in
-//         the A-operand layout (row = head l%16, k = token 4(l/16) + r), and
+//         the A-operand layout (row = l%16, k = token 4(l/16) + r), and
 //         round r of V loads token 4(l/16) + r, 16 bytes per lane, so each of
 //         the lane's 8 elements is the B operand of one MFMA.  V never needs
 //         a transpose; P stays fp32 (no rounding of the weights to 16 bits).
 //
 // VALU work per tile is reduced to the 16-bit -> fp32 conversion of V and the
-// softmax bookkeeping, independent of G.
+// softmax bookkeeping, independent of the row count.
 //
 // Compiled once per (element type, head size): PDA_DTYPE (0 bf16, 1 fp16)
 // and PDA_HEAD (64, 128, 256).
@@ -82,14 +84,18 @@ __device__ inline float sum_token_groups(float x) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// NG = 0: PV on v_mfma_f32_16x16x4_f32 with the group padded to 16 heads.
-// NG = 1, 2: PV on v_mfma_f32_4x4x1_16b_f32, NG groups of 4 heads: block
-// (lanes 4k..4k+3) = one token (the lane's V row of the round) x 4 columns
-// of d, rows = the 4 heads of a group; no padding to 16, a quarter of the
-// matrix-core cycles per head group.  Each lane group (l / 16) accumulates
+// The unit's R = q_len * G rows (row r: query position r / G, head r % G)
+// are packed in RC chunks of 16 (RC = 2 for R > 16): each K tile feeds RC
+// QK products, and each chunk keeps its own softmax state and accumulators.
+// NG = 0: PV on v_mfma_f32_16x16x4_f32 with each chunk padded to 16 rows.
+// NG = 1, 2 (R <= 8, RC = 1): PV on v_mfma_f32_4x4x1_16b_f32, NG blocks of 4
+// rows: block (lanes 4k..4k+3) = one token (the lane's V row of the round) x
+// 4 columns of d, rows = the 4 rows of a block; no padding to 16, a quarter
+// of the matrix-core cycles per block.  Each lane group (l / 16) accumulates
 // over its own tokens; the four partial sums are added once at the end.
-template <typename Elt, int D, bool ALIGNED, bool BUF, int NG>
+template <typename Elt, int D, bool ALIGNED, bool BUF, int NG, int RC>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+    static_assert(RC == 1 || (RC == 2 && NG == 0), "two row chunks use the padded PV form");
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
     extern __shared__ float smem[];
@@ -100,22 +106,25 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int q4 = lane >> 4, c16 = lane & 15;
-    const int G = p.group;
+    const int R = p.rows;
 
     // Loads that do not depend on the context length leave together with the
     // seq_lens load, so the first K/V loads wait for one round trip, not three:
-    // Q^T, the B operand (head c16 of the group, elements 32s + 8*q4 .. +8 for
-    // k-step s; lanes past G read head G-1 again, and the results of those
-    // padding heads are never written), and on the aligned path the table
-    // entries of the wave's first two tiles at the partition's start without
-    // a sliding window.
+    // Q^T, the B operand of chunk c (row 16c + c16 of the unit, elements
+    // 32s + 8*q4 .. +8 for k-step s; lanes past R read row R-1 again, and the
+    // results of those padding rows are never written), and on the aligned
+    // path the table entries of the wave's first two tiles at the partition's
+    // start without a sliding window.
     const int raw_len = p.seq_lens[b];
-    uint4 qb[KS];
-    {
-        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                               ((int64_t)b * p.num_q_heads + g * G + min(c16, G - 1)) * D + 8 * q4;
+    int lrow[RC];  // the lane's row in each chunk (clamped to a real row)
+    uint4 qb[RC][KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qb[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+    for (int c = 0; c < RC; ++c) {
+        lrow[c] = min(16 * c + c16, R - 1);
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(p.q) + row_index(p, b, g, lrow[c]) * D + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qb[c][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
     }
     const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
     TileBlock first[2] = {{0, 0}, {0, 0}};
@@ -138,6 +147,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         if (part == 0) zero_unit_rows<D>(p, b, g);
         return;
     }
+    RowRange rr[RC];  // tokens the lane's row of each chunk attends to
+#pragma unroll
+    for (int c = 0; c < RC; ++c) rr[c] = row_range(p, rg, lrow[c] / p.group);
     const int t1 = min(t0 + p.tokens_per_part, L);
     const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
     const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
@@ -208,10 +220,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         return ALIGNED ? tile_block(p, trow, tile_start(jj)) : TileBlock{0, 0};
     };
 
-    // NG = 0: oacc[0][dh][e][r] = O[head 4*q4 + r][d = dh*128 + 8*c16 + e]
-    // NG > 0: oacc[grp][dh][e][i] = O[head 4*grp + i][same d], partial over
+    // NG = 0: oacc[c][dh][e][r] = O[row 16c + 4*q4 + r][d = dh*128 + 8*c16 + e]
+    // NG > 0: oacc[grp][dh][e][i] = O[row 4*grp + i][same d], partial over
     //         the tokens of lane group q4
-    constexpr int NA = NG == 0 ? 1 : NG;
+    constexpr int NA = NG == 0 ? RC : NG;
     f32x4_t oacc[NA][DH][8];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
@@ -219,75 +231,95 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
             for (int e = 0; e < 8; ++e) oacc[a][dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = -FLT_MAX;  // running max of head c16 (finite floor: exp2(-inf - m) = 0)
-    float l = 0.f;       // this lane's share of head c16's denominator
+    float m[RC], l[RC];
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+        m[c] = -FLT_MAX;  // running max of row 16c + c16 (finite floor: exp2(-inf - m) = 0)
+        l[c] = 0.f;       // this lane's share of that row's denominator
+    }
 
     auto process = [&](int j, const uint4 (&kr)[KS], const uint4 (&vr)[4][DH]) {
         const int tile_base = t0 + j * TT;
-        const bool full = tile_base >= rg.lo && tile_base + TT <= t1;
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        const bool full = full_tile(rg, tile_base, TT, t1);
+        float sc[RC][4];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(kr[s], qb[s], sacc);
-        float sc[4];
+        for (int c = 0; c < RC; ++c) {
+            f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = sacc[r] * p.scale_log2;
+            for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(kr[s], qb[c][s], sacc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[c][r] = sacc[r] * p.scale_log2;
+        }
         if (!full) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = tile_base + mfma_v_offset(lane, r);
-                sc[r] = (t >= rg.lo && t < t1) ? sc[r] : -INFINITY;
-            }
+            for (int c = 0; c < RC; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = tile_base + mfma_v_offset(lane, r);
+                    sc[c][r] = (t >= rr[c].lo && t < min(t1, rr[c].end)) ? sc[c][r] : -INFINITY;
+                }
         }
-        float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        if (__builtin_amdgcn_ballot_w64(mn > m)) {
-            const float alpha = fast_exp2(m - mn);
-            l *= alpha;
-            if constexpr (NG == 0) {
-                // the accumulator rows of this lane are heads 4*q4 + r
-                float ar[4];
+        float mn[RC];
+        bool grew = false;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+        for (int c = 0; c < RC; ++c) {
+            float mt = fmaxf(fmaxf(sc[c][0], sc[c][1]), fmaxf(sc[c][2], sc[c][3]));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mn[c] = fmaxf(m[c], mt);
+            grew |= mn[c] > m[c];
+        }
+        if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
-                for (int dh = 0; dh < DH; ++dh)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) oacc[0][dh][e][r] *= ar[r];
-            } else {
-                // heads 4*grp + i: their factors sit in lanes 4*grp + i
-#pragma unroll
-                for (int grp = 0; grp < NG; ++grp) {
+            for (int c = 0; c < RC; ++c) {
+                const float alpha = fast_exp2(m[c] - mn[c]);
+                l[c] *= alpha;
+                if constexpr (NG == 0) {
+                    // the accumulator rows of this lane are rows 16c + 4*q4 + r
                     float ar[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        ar[i] = __int_as_float(
-                            __builtin_amdgcn_readlane(__float_as_int(alpha), 4 * grp + i));
+                    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
 #pragma unroll
                     for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) oacc[grp][dh][e][i] *= ar[i];
-                }
-            }
-            m = mn;
-        }
-        float pr[4];
+                            for (int r = 0; r < 4; ++r) oacc[c][dh][e][r] *= ar[r];
+                } else {
+                    // rows 4*grp + i: their factors sit in lanes 4*grp + i
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pr[r] = fast_exp2(sc[r] - m);
-            l += pr[r];
+                    for (int grp = 0; grp < NG; ++grp) {
+                        float ar[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            ar[i] = __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(alpha), 4 * grp + i));
+#pragma unroll
+                        for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) oacc[grp][dh][e][i] *= ar[i];
+                    }
+                }
+                m[c] = mn[c];
+            }
         }
-        // A operand of the 4-head blocks: lane 4k + i needs head 4*grp + i
-        float pa[NA][4];
+        float pr[RC][4];
+#pragma unroll
+        for (int c = 0; c < RC; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[c][r] = fast_exp2(sc[c][r] - m[c]);
+                l[c] += pr[c][r];
+            }
+        // A operand of the 4-row blocks: lane 4k + i needs row 4*grp + i
+        float pa[NG > 0 ? NG : 1][4];
         if constexpr (NG > 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pa[0][r] = take_head_of_group<0>(pr[r]);
-                if constexpr (NG > 1) pa[1][r] = take_head_of_group<1>(pr[r]);
+                pa[0][r] = take_head_of_group<0>(pr[0][r]);
+                if constexpr (NG > 1) pa[1][r] = take_head_of_group<1>(pr[0][r]);
             }
         }
 #pragma unroll
@@ -302,9 +334,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
                 if constexpr (NG == 0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        oacc[0][dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            pr[r], vf[e], oacc[0][dh][e], 0, 0, 0);
+                    for (int c = 0; c < RC; ++c)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            oacc[c][dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                pr[c][r], vf[e], oacc[c][dh][e], 0, 0, 0);
                 } else {
 #pragma unroll
                     for (int grp = 0; grp < NG; ++grp)
@@ -336,9 +370,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         load_tile(j + 3 * kWaves, block_of(j + 3 * kWaves), kb, vb);
     }
 
-    // full denominator of head c16 (all four lane groups hold the same m)
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    // full denominator of each lane row (all four lane groups hold the same m)
+#pragma unroll
+    for (int c = 0; c < RC; ++c) {
+        l[c] += __shfl_xor(l[c], 16);
+        l[c] += __shfl_xor(l[c], 32);
+    }
     if constexpr (NG > 0) {  // add the four lane groups' partial sums
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp)
@@ -351,22 +388,24 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                         oacc[grp][dh][e][i] = sum_token_groups(oacc[grp][dh][e][i]);
     }
 
-    // merge the wavefronts and write the unit's result, heads in chunks
-    for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
-        const int hn = min(kHeadChunk, G - h0);
+    // merge the wavefronts and write the unit's result, rows in chunks
+    for (int h0 = 0; h0 < R; h0 += kHeadChunk) {
+        const int hn = min(kHeadChunk, R - h0);
         if constexpr (NG == 0) {
             if (c16 < CW) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int hi = 4 * q4 + r - h0;
-                    if (hi < 0 || hi >= hn) continue;
-                    float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+                for (int c = 0; c < RC; ++c)
 #pragma unroll
-                    for (int dh = 0; dh < DH; ++dh)
+                    for (int r = 0; r < 4; ++r) {
+                        const int hi = 16 * c + 4 * q4 + r - h0;
+                        if (hi < 0 || hi >= hn) continue;
+                        float* row = red + (wave * kHeadChunk + hi) * (D + 2);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            row[dh * 128 + 8 * c16 + e] = oacc[0][dh][e][r];
-                }
+                        for (int dh = 0; dh < DH; ++dh)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                row[dh * 128 + 8 * c16 + e] = oacc[c][dh][e][r];
+                    }
             }
         } else {
             if (q4 == 0 && c16 < CW) {
@@ -385,14 +424,19 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                     }
             }
         }
-        if (q4 == 0 && c16 >= h0 && c16 < h0 + hn) {
-            float* row = red + (wave * kHeadChunk + c16 - h0) * (D + 2);
-            row[D] = m;
-            row[D + 1] = l;
+        if (q4 == 0) {
+#pragma unroll
+            for (int c = 0; c < RC; ++c) {
+                const int hi = 16 * c + c16 - h0;
+                if (hi < 0 || hi >= hn) continue;
+                float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+                row[D] = m[c];
+                row[D + 1] = l[c];
+            }
         }
         __syncthreads();
         write_unit_rows<Elt, D>(p, red, kHeadChunk, h0, hn, b, g, part);
-        if (h0 + kHeadChunk < G) __syncthreads();  // before the next chunk reuses red
+        if (h0 + kHeadChunk < R) __syncthreads();  // before the next chunk reuses red
     }
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
@@ -404,32 +448,34 @@ using EltT = FP16;
 #endif
 constexpr int kHead = PDA_HEAD;
 
-template <bool ALIGNED, bool BUF, int NG>
+template <bool ALIGNED, bool BUF, int NG, int RC>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
     const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG>), grid,
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC>), grid,
                               dim3(kThreads), lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG>), grid,
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC>), grid,
                            dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 
-// PV form by group size: 4-head blocks for up to 4 heads, and for up to 8
+// PV form by rows per unit: 4-row blocks for up to 4 rows, and for up to 8
 // at head sizes up to 128, where they take at most half the matrix-core
-// cycles of the padded 16-head form; the padded form otherwise (two 4-head
-// groups at head size 256 need more registers than a wave has: their
-// accumulators hold four token-group partials per output).
+// cycles of the padded 16-row form; the padded form otherwise (two 4-row
+// blocks at head size 256 need more registers than a wave has: their
+// accumulators hold four token-group partials per output), in two chunks
+// beyond 16 rows.
 template <bool ALIGNED, bool BUF>
 static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-    if (p.group <= 4) return launch_one<ALIGNED, BUF, 1>(p, batch, stream, start, stop);
+    if (p.rows <= 4) return launch_one<ALIGNED, BUF, 1, 1>(p, batch, stream, start, stop);
     if constexpr (kHead <= 128)
-        if (p.group <= 8) return launch_one<ALIGNED, BUF, 2>(p, batch, stream, start, stop);
-    return launch_one<ALIGNED, BUF, 0>(p, batch, stream, start, stop);
+        if (p.rows <= 8) return launch_one<ALIGNED, BUF, 2, 1>(p, batch, stream, start, stop);
+    if (p.rows <= 16) return launch_one<ALIGNED, BUF, 0, 1>(p, batch, stream, start, stop);
+    return launch_one<ALIGNED, BUF, 0, 2>(p, batch, stream, start, stop);
 }
 
 #define PDA_CAT2(a, b, c) a##_##b##_##c

@@ -1,17 +1,19 @@
 // Paged-attention decode, VALU variant, for gfx950.
 //
 // One workgroup (4 wavefronts) per unit (partition p, KV head g, sequence b).
-// All G query heads of the KV group are packed in the unit, so every K/V
-// byte of the partition is read from HBM once.  Each lane loads 16 contiguous
+// All rows of the unit are packed (the G query heads of the KV group, for
+// each of the q_len query positions), so every K/V byte of the partition is
+// read from HBM once.  Each lane loads 16 contiguous
 // bytes of a token row; a row spans D/8 lanes, so a wavefront load covers
 // whole rows and consecutive lanes touch consecutive addresses.
 //
 // Per tile and lane:
 //   QK^T   packed dot2 over the lane's 8 elements, then a DPP sum over the
-//          row's lanes -> one score per packed head;
-//   mask   scores of tokens at or past the partition end are replaced by -inf
-//          with a select (tail slots are not even addressed: see
-//          locate_token), so NaN or garbage there cannot reach a score;
+//          token row's lanes -> one score per packed row;
+//   mask   scores of tokens at or past the partition end, outside a sliding
+//          window or after a row's causal end are replaced by -inf with a
+//          select (tail slots are not even addressed: see tile_row), so NaN
+//          or garbage there cannot reach a score;
 //   online softmax in the exp2 domain, per lane sub-stream, with a rescale
 //          only when some lane's running max grew;
 //   PV     fp32 FMAs of the lane's 8 V elements.
@@ -46,7 +48,7 @@ namespace pda {
 template <typename Elt, int D, int GP, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     using Geo = ValuGeom<D>;
-    constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U, TT = Geo::TT;
+    constexpr int LPT = Geo::LPT, RT = Geo::R, U = Geo::U, TT = Geo::TT;
     extern __shared__ float smem[];
     float* red = smem;                                                  // [kWaves][GP][D+2]
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
@@ -55,25 +57,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int c = lane % LPT, r = lane / LPT;
-    const int G = p.group;
+    const int R = p.rows;  // rows of the unit: q_len positions x G heads
     constexpr int S = PDA_VALU_STAGES;
     static_assert(S >= 2 && S <= 8, "stages");
 
     // Loads that do not depend on the context length leave together with the
     // seq_lens load, so the first K/V loads wait for one round trip, not
-    // three: the packed query rows of this KV group (8 elements per lane and
-    // head; padding heads past G read head G-1 again, and their results are
-    // never written), and on the aligned path the table entries of the
-    // wave's first S-1 tiles at the partition's start without a sliding
-    // window.
+    // three: the packed query rows of this unit (8 elements per lane and row;
+    // padding rows past R read row R-1 again, and their results are never
+    // written), and on the aligned path the table entries of the wave's
+    // first S-1 tiles at the partition's start without a sliding window.
     const int raw_len = p.seq_lens[b];
     uint4 qv[GP];
-    {
-        const uint16_t* qb = static_cast<const uint16_t*>(p.q) +
-                             ((int64_t)b * p.num_q_heads + g * G) * D + c * 8;
 #pragma unroll
-        for (int i = 0; i < GP; ++i)
-            qv[i] = *reinterpret_cast<const uint4*>(qb + (int64_t)min(i, G - 1) * D);
+    for (int i = 0; i < GP; ++i) {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                               row_index(p, b, g, min(i, R - 1)) * D + c * 8;
+        qv[i] = *reinterpret_cast<const uint4*>(qrow);
     }
     const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
     static_assert(S == 3, "the first-tile table entries are kept for S - 1 = 2 tiles");
@@ -97,6 +97,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         if (part == 0) zero_unit_rows<D>(p, b, g);
         return;
     }
+    RowRange rr[GP];  // tokens each row attends to
+#pragma unroll
+    for (int i = 0; i < GP; ++i) rr[i] = row_range(p, rg, min(i, R - 1) / p.group);
     const int t1 = min(t0 + p.tokens_per_part, L);
     const int lb0 = (int)fastdiv((uint32_t)t0, p.bs_div);
     const int lb1 = (int)fastdiv((uint32_t)(t1 - 1), p.bs_div);
@@ -139,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         for (int u = 0; u < U; ++u) {
             int phys = tb.phys, slot0 = tb.slot0, dt;
             if constexpr (ALIGNED)
-                dt = tile_row(tile_base, rg.lo, t1, u * R + r);
+                dt = tile_row(tile_base, rg.lo, t1, u * RT + r);
             else
-                locate_token<R, false>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0, dt);
+                locate_token<RT, false>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0, dt);
             const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (2 * D) + lane_off;
             if constexpr (kBuf) {
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // One tile of QK^T, masking, online softmax and PV for this lane.
     auto process = [&](int j, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
         const int tile_base = t0 + j * TT;
-        const bool full = tile_base >= rg.lo && tile_base + TT <= t1;
+        const bool full = full_tile(rg, tile_base, TT, t1);
         float s[U][GP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -185,10 +188,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         if (!full) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int t = tile_base + u * R + r;
-                const bool valid = t >= rg.lo && t < t1;
+                const int t = tile_base + u * RT + r;
 #pragma unroll
-                for (int i = 0; i < GP; ++i) s[u][i] = valid ? s[u][i] : -INFINITY;
+                for (int i = 0; i < GP; ++i)
+                    s[u][i] = (t >= rr[i].lo && t < min(t1, rr[i].end)) ? s[u][i] : -INFINITY;
             }
         }
         bool grew = false;
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         }
     }
 
-    // merge the R lane sub-streams (lanes c, c+LPT, ...) of the wavefront
+    // merge the RT lane sub-streams (lanes c, c+LPT, ...) of the wavefront
 #pragma unroll
     for (int x = LPT; x < kWave; x <<= 1) {
 #pragma unroll
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     __syncthreads();
 
     // merge the wavefronts and write the unit's result
-    write_unit_rows<Elt, D>(p, red, GP, 0, G, b, g, part);
+    write_unit_rows<Elt, D>(p, red, GP, 0, R, b, g, part);
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
 

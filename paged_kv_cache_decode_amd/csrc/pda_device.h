@@ -179,22 +179,49 @@ __device__ inline int context_len(const DecodeParams& p, int b) {
     return max(0, min(p.seq_lens[b], p.max_seq_len));
 }
 
-// Tokens of sequence b the decode attends to: [lo, L), lo = max(0, L - W)
-// for a sliding window W > 0, else 0.  The partitions tile [base, L) with
-// base = lo rounded down to the 16-token grid, so that aligned tiles keep
-// starting on it; rows in [base, lo) are redirected to lo (tile_row) and
-// their scores are masked, so no slot before the window is ever read.
+// Tokens of sequence b the decode attends to.  With n = q_len query rows,
+// row i attends to [lo_i, e_i), e_i = L - n + i + 1 (causal among the new
+// rows; e_{n-1} = L), lo_i = max(0, e_i - W) for a sliding window W > 0,
+// else 0.  The unit reads [lo, L) with lo = lo_0, the smallest; its
+// partitions tile [base, L) with base = lo rounded down to the 16-token grid,
+// so that aligned tiles keep starting on it; rows in [base, lo) are
+// redirected to lo (tile_row) and their scores are masked, so no slot before
+// the window is ever read.  end0 = e_0 and lo_last = lo_{n-1} bound the
+// tiles every row takes whole (full_tile).
 // seq_range_of takes the raw seq_lens entry, loaded by the caller.
 struct SeqRange {
-    int L, lo, base;
+    int L, lo, base, end0, lo_last;
 };
 __device__ inline SeqRange seq_range_of(const DecodeParams& p, int raw_len) {
     const int L = max(0, min(raw_len, p.max_seq_len));
-    const int lo = p.window > 0 ? max(0, L - p.window) : 0;
-    return SeqRange{L, lo, lo & ~(kAlignTokens - 1)};
+    const int end0 = L - p.q_len + 1;
+    const int lo = p.window > 0 ? max(0, end0 - p.window) : 0;
+    const int lo_last = p.window > 0 ? max(0, L - p.window) : 0;
+    return SeqRange{L, lo, lo & ~(kAlignTokens - 1), end0, lo_last};
 }
 __device__ inline SeqRange seq_range(const DecodeParams& p, int b) {
     return seq_range_of(p, p.seq_lens[b]);
+}
+
+// Tokens [lo, end) of query row position i (see SeqRange).
+struct RowRange {
+    int lo, end;
+};
+__device__ inline RowRange row_range(const DecodeParams& p, const SeqRange& rg, int i) {
+    const int end = rg.end0 + i;
+    return RowRange{p.window > 0 ? max(0, end - p.window) : 0, end};
+}
+// Whether every row attends to every token of [tile_base, tile_base + tt)
+// (tokens below t1, the partition end): no score of the tile needs a mask.
+__device__ inline bool full_tile(const SeqRange& rg, int tile_base, int tt, int t1) {
+    return tile_base >= rg.lo_last && tile_base + tt <= min(t1, rg.end0);
+}
+
+// Row r of a unit (b, g) packs query position i = r / G and head h = r % G;
+// its index among the [B][q_len][Hq] rows of q, out and the partials.
+__device__ inline int64_t row_index(const DecodeParams& p, int b, int g, int r) {
+    const int i = r / p.group, h = r - i * p.group;
+    return ((int64_t)b * p.q_len + i) * p.num_q_heads + g * p.group + h;
 }
 
 // A compiler barrier for memory operations, emitting no instruction and no
@@ -305,7 +332,7 @@ __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + 
 
 
 // ---- unit epilogue shared by the decode kernels ------------------------
-// Combine the kWaves per-wave states of heads h0 .. h0+hn-1 of unit (b, g),
+// Combine the kWaves per-wave states of rows h0 .. h0+hn-1 of unit (b, g),
 // staged in LDS as red[w][i][0..D) = unnormalised O, red[w][i][D] = running
 // max m (exp2 domain), red[w][i][D+1] = denominator l, in a fixed order, and
 // write either the 16-bit output (one partition) or the fp32 partial.
@@ -327,19 +354,23 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
             den += row[D + 1] * wt;
             o += row[d] * wt;
         }
-        const int h = g * p.group + h0 + i;
+        // a row with no token in this partition (a causal row ending before
+        // it) has den == 0: its normalised partial is 0, and its weight l = 0
+        // keeps it out of the merge
+        const float on = den > 0.f ? o / den : 0.f;
+        const int64_t row = row_index(p, b, g, h0 + i);
         if (direct) {
-            out16[((int64_t)b * p.num_q_heads + h) * D + d] = Elt::from_float(o / den);
+            out16[row * D + d] = Elt::from_float(on);
         } else {
-            const int64_t prow = ((int64_t)b * p.num_q_heads + h) * p.num_partitions + part;
+            const int64_t prow = row * p.num_partitions + part;
             if (p.fused_merge) {  // read back by another workgroup of this launch
-                store_coherent(p.ws_o + prow * D + d, o / den);
+                store_coherent(p.ws_o + prow * D + d, on);
                 if (d == 0) {
                     store_coherent(p.ws_ml + prow * 2, M);
                     store_coherent(p.ws_ml + prow * 2 + 1, den);
                 }
             } else {              // read by the merge kernel after this launch
-                p.ws_o[prow * D + d] = o / den;
+                p.ws_o[prow * D + d] = on;
                 if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
             }
         }
@@ -347,16 +378,16 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
 }
 
 // Log-sum-exp merge of the Pb partials (o_p normalised, m_p, l_p in the exp2
-// domain) of the G heads of unit (b, g), one output element per thread and
+// domain) of the R rows of unit (b, g), one output element per thread and
 // step, partitions in index order with a running max:
-//   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p.
+//   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p
+// (0 for a row with no token at all).
 template <typename Elt, int D>
 __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
     uint16_t* out16 = static_cast<uint16_t*>(p.out);
-    const int G = p.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < p.rows * D; idx += blockDim.x) {
         const int i = idx / D, d = idx - i * D;
-        const int64_t row = (int64_t)b * p.num_q_heads + g * G + i;
+        const int64_t row = row_index(p, b, g, i);
         const float* ml = p.ws_ml + row * p.num_partitions * 2;
         const float* po = p.ws_o + row * p.num_partitions * D + d;
         float M = -FLT_MAX, o = 0.f, den = 0.f;
@@ -371,7 +402,7 @@ __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
             den = den * sc + w;
             M = mn;
         }
-        out16[row * D + d] = Elt::from_float(o / den);
+        out16[row * D + d] = Elt::from_float(den > 0.f ? o / den : 0.f);
     }
 }
 
@@ -399,12 +430,14 @@ __device__ inline void fused_merge_tail(const DecodeParams& p, const SeqRange& r
     if (s_last) merge_unit<Elt, D>(p, b, g, Pb);
 }
 
-// Zero output rows of the G heads of (b, g) (an empty context).
+// Zero output rows of the R rows of (b, g) (an empty context).
 template <int D>
 __device__ inline void zero_unit_rows(const DecodeParams& p, int b, int g) {
     uint16_t* out16 = static_cast<uint16_t*>(p.out);
-    for (int idx = threadIdx.x; idx < p.group * D; idx += blockDim.x)
-        out16[((int64_t)b * p.num_q_heads + g * p.group) * D + idx] = 0;
+    for (int idx = threadIdx.x; idx < p.rows * D; idx += blockDim.x) {
+        const int i = idx / D, d = idx - i * D;
+        out16[row_index(p, b, g, i) * D + d] = 0;
+    }
 }
 
 }  // namespace pda

@@ -84,11 +84,19 @@ int64_t table_capacity(const pda_shape_t* s, const pda_plan_t* pl) {
     return (int64_t)pl->tokens_per_partition / s->block_size + 2;
 }
 
-// Tokens a partition grid must cover: the whole context, or a sliding
-// window rounded out to the 16-token grid its partitions start on.
+// Query rows per sequence (0 is read as 1) and rows per unit.
+int64_t q_len_of(const pda_shape_t* s) { return s->q_len > 1 ? s->q_len : 1; }
+int64_t rows_of(const pda_shape_t* s) {
+    return q_len_of(s) * (s->num_q_heads / s->num_kv_heads);
+}
+
+// Tokens a partition grid must cover: the whole context, or the union of
+// the rows' sliding windows rounded out to the 16-token grid its partitions
+// start on.
 int64_t plan_span(const pda_shape_t* s) {
     if (s->sliding_window > 0)
-        return std::min<int64_t>(s->max_seq_len, (int64_t)s->sliding_window + kAlignTokens - 1);
+        return std::min<int64_t>(s->max_seq_len, (int64_t)s->sliding_window + q_len_of(s) - 1 +
+                                                     kAlignTokens - 1);
     return s->max_seq_len;
 }
 
@@ -102,10 +110,10 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
     if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen)
         return PDA_ERR_UNSUPPORTED;
     if (pl->merge != PDA_MERGE_FUSED && pl->merge != PDA_MERGE_KERNEL) return PDA_ERR_INVALID;
-    const int G = s->num_q_heads / s->num_kv_heads;
+    const int R = (int)rows_of(s);
     if (pl->variant == PDA_VARIANT_VALU) {
-        if (G > kValuMaxGroup) return PDA_ERR_UNSUPPORTED;
-        const int64_t lds = (int64_t)decode_lds_bytes(s->head_size, valu_group_pad(G),
+        if (R > kValuMaxGroup) return PDA_ERR_UNSUPPORTED;
+        const int64_t lds = (int64_t)decode_lds_bytes(s->head_size, valu_group_pad(R),
                                                       (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else if (pl->variant == PDA_VARIANT_MFMA) {
@@ -144,6 +152,8 @@ DecodeParams make_params(const pda_shape_t* s, const pda_plan_t* pl, float scale
     p.max_blocks_per_seq = s->max_blocks_per_seq;
     p.max_seq_len = s->max_seq_len;
     p.window = s->sliding_window;
+    p.q_len = (int32_t)q_len_of(s);
+    p.rows = (int32_t)rows_of(s);
     p.num_blocks = s->num_blocks;
     p.num_partitions = pl->num_partitions;
     p.tokens_per_part = pl->tokens_per_partition;
@@ -165,18 +175,19 @@ int pda_check_shape(const pda_shape_t* s) {
     if (!s) return PDA_ERR_INVALID;
     if (s->num_seqs < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->block_size < 1 ||
         s->num_blocks < 1 || s->max_blocks_per_seq < 1 || s->max_seq_len < 0 ||
-        s->sliding_window < 0)
+        s->sliding_window < 0 || s->q_len < 0)
         return PDA_ERR_INVALID;
     if (s->num_q_heads % s->num_kv_heads != 0) return PDA_ERR_INVALID;
     if (s->head_size != 64 && s->head_size != 128 && s->head_size != 256)
         return PDA_ERR_UNSUPPORTED;
     if (s->dtype != PDA_BF16 && s->dtype != PDA_FP16) return PDA_ERR_UNSUPPORTED;
     if (s->num_q_heads / s->num_kv_heads > PDA_MAX_GROUP) return PDA_ERR_UNSUPPORTED;
+    if (s->q_len > PDA_MAX_ROWS || rows_of(s) > PDA_MAX_ROWS) return PDA_ERR_UNSUPPORTED;
     if ((int64_t)s->max_seq_len > (int64_t)s->max_blocks_per_seq * s->block_size)
         return PDA_ERR_INVALID;
     if (s->max_seq_len > kMaxSeqLen) return PDA_ERR_UNSUPPORTED;
     if (s->num_seqs > kMaxGridYZ || s->num_kv_heads > kMaxGridYZ ||
-        s->num_q_heads > kMaxGridYZ)
+        s->num_q_heads > kMaxGridYZ || (int64_t)s->num_seqs * q_len_of(s) > kMaxGridYZ)
         return PDA_ERR_UNSUPPORTED;
     return PDA_OK;
 }
@@ -186,10 +197,10 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     if (rc != PDA_OK) return rc;
     if (!plan || cu_count < 1) return PDA_ERR_INVALID;
     // the rule documented in pda.h
-    const int64_t G = s->num_q_heads / s->num_kv_heads;
+    const int64_t R = rows_of(s);
     const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
-    const bool mfma = G > PDA_VALU_MAX_GROUP ||
-                      (G >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
+    const bool mfma = R > PDA_VALU_MAX_GROUP ||
+                      (R >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
     const int64_t bpt = 4 * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
     const int64_t t_min = std::max(align, (PDA_WG_MIN_BYTES / bpt / align) * align);
@@ -216,7 +227,7 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
 int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
     if (!s || !pl) return PDA_ERR_INVALID;
     if (pl->num_partitions <= 1) return 0;
-    const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
+    const int64_t rows = (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
     return round256(rows * s->head_size * 4) + round256(rows * 2 * 4) +
            round256((int64_t)s->num_seqs * s->num_kv_heads * 4);
 }
@@ -265,7 +276,8 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
     p.seq_lens = seq_lens;
     p.out = out;
     if (need > 0) {
-        const int64_t rows = (int64_t)s->num_seqs * s->num_q_heads * pl->num_partitions;
+        const int64_t rows =
+            (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
         char* ws = static_cast<char*>(workspace);
         const int64_t o_bytes = round256(rows * s->head_size * 4);
         const int64_t ml_bytes = round256(rows * 2 * 4);
@@ -275,16 +287,15 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
         p.fused_merge = pl->merge == PDA_MERGE_FUSED;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int G = p.group;
     const bool aligned = block_aligned(s);
     hipError_t e = pl->variant == PDA_VARIANT_MFMA
                        ? launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
                                             ev0, ev1)
-                       : launch_decode_valu(s->dtype, s->head_size, valu_group_pad(G), aligned, p,
-                                            s->num_seqs, st, ev0, ev1);
+                       : launch_decode_valu(s->dtype, s->head_size, valu_group_pad(p.rows),
+                                            aligned, p, s->num_seqs, st, ev0, ev1);
     if (e != hipSuccess) return PDA_ERR_LAUNCH;
     if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
-        e = launch_merge(s->dtype, s->head_size, p, s->num_seqs, st);
+        e = launch_merge(s->dtype, s->head_size, p, (int)(s->num_seqs * q_len_of(s)), st);
         if (e != hipSuccess) return PDA_ERR_LAUNCH;
     }
     return PDA_OK;
@@ -369,7 +380,7 @@ const char* pda_status_string(int status) {
 #define PDA_BUILD_FLAGS "unknown"
 #endif
 const char* pda_build_id(void) {
-    return "libpda 0.2.0; target gfx950; variants valu|mfma; merge fused|kernel; flags " PDA_BUILD_FLAGS;
+    return "libpda 0.3.0; target gfx950; variants valu|mfma; merge fused|kernel; flags " PDA_BUILD_FLAGS;
 }
 
 }  // extern "C"

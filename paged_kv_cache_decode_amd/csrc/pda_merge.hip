@@ -6,13 +6,15 @@
 // p of query head h left a normalised fp32 output o_p, its max score m_p (exp2
 // domain) and its denominator l_p.  The exact softmax over the union is
 //     M = max_p m_p,   w_p = l_p * 2^(m_p - M),   out = sum_p w_p o_p / sum_p w_p
-// over the partitions that hold tokens (p < ceil(L / T_p)); the stale
-// workspace entries of empty partitions may be loaded but never enter the
-// sums.  L == 0 gives a zero row.
+// over the partitions that hold tokens (p < ceil((L - base) / T_p)); the
+// stale workspace entries of empty partitions may be loaded but never enter
+// the sums.  A partition in which a causal row has no token left l_p = 0,
+// so it weighs nothing; a row with no token at all (L == 0, or L < q_len)
+// gives zeros.
 //
 // One workgroup of 256 threads per (64-element chunk of D, query head,
-// sequence): 16 lanes x 4 elements cover the chunk, 16 partition groups
-// stride over p.  Each thread merges its partitions with a running max, a
+// query row position and sequence): 16 lanes x 4 elements cover the chunk,
+// 16 partition groups stride over p.  Each thread merges its partitions with a running max, a
 // batch of loads at a time; the 16 groups are then combined in a fixed order
 // through LDS, so the result does not depend on timing.
 #include "pda_device.h"
@@ -24,9 +26,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     constexpr int kBatch = 8;  // partitions per thread and memory round trip
     __shared__ float4 red_o[16][16];
     __shared__ float2 red_mw[16][16];
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int chunk = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;  // bi = b * q_len + i
+    const int b = bi / p.q_len;
     const int tid = threadIdx.x, d4 = tid & 15, pg = tid >> 4;
-    const int64_t row = (int64_t)b * p.num_q_heads + h;
+    const int64_t row = (int64_t)bi * p.num_q_heads + h;
     uint16_t* out = static_cast<uint16_t*>(p.out) + row * D + chunk * 64 + d4 * 4;
     const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + row * p.num_partitions;
     const float* po = p.ws_o + row * p.num_partitions * D + chunk * 64 + d4 * 4;
@@ -109,13 +112,15 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
             s.x += f * t.x; s.y += f * t.y; s.z += f * t.z; s.w += f * t.w;
             ws += f * mw.y;
         }
-        out[0] = Elt::from_float(s.x / ws);
-        out[1] = Elt::from_float(s.y / ws);
-        out[2] = Elt::from_float(s.z / ws);
-        out[3] = Elt::from_float(s.w / ws);
+        // a row with no token at all has ws == 0: zeros
+        out[0] = Elt::from_float(ws > 0.f ? s.x / ws : 0.f);
+        out[1] = Elt::from_float(ws > 0.f ? s.y / ws : 0.f);
+        out[2] = Elt::from_float(ws > 0.f ? s.z / ws : 0.f);
+        out[3] = Elt::from_float(ws > 0.f ? s.w / ws : 0.f);
     }
 }
 
+// batch: B * q_len (grid z runs over sequences and their query positions)
 template <typename Elt, int D>
 static hipError_t launch_merge_t(const DecodeParams& p, int batch, hipStream_t stream) {
     const dim3 grid(D / 64, p.num_q_heads, batch);

@@ -34,6 +34,8 @@ def run(case: kvgen.Case, plan=None, out=None) -> torch.Tensor:
 
 def reference(case: kvgen.Case, seqs=None) -> np.ndarray:
     q, k, v, lens = kvgen.oracle_inputs(case, seqs)
+    if case.q_len > 1:
+        return oracle.decode_multi(q, k, v, lens, case.scale, window=case.sliding_window)
     return oracle.decode(q, k, v, lens, case.scale, window=case.sliding_window)
 
 

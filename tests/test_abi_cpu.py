@@ -50,11 +50,15 @@ def test_plan_matches_oracle_plan(D):
         mbs = max(1, -(-L // bs))
         cu = int(rng.choice([1, 7, 80, 256, 304]))
         W = int(rng.choice([0, 0, 1, 31, 1024]))
-        shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16", sliding_window=W)
+        n = int(rng.choice([1, 1, 2, 3, 8]))
+        if n * G > 32:
+            n = 1
+        shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16", sliding_window=W,
+                               q_len=n)
         got = pda.pda_plan_for_cus(shape, cu)
-        P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W)
+        P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n)
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
-        assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv)
+        assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv, q_len=n)
         assert got.merge == pda.PDA_MERGE_KERNEL
         assert got.cu_count == cu
 
@@ -66,7 +70,7 @@ def test_plan_golden_through_library():
     for c in g["cases"]:
         shape = pda.make_shape(c["B"], c["Hkv"] * c["G"], c["Hkv"], c["D"], 16, 1,
                                max(1, -(-c["Lmax"] // 16)), c["Lmax"],
-                               sliding_window=c.get("W", 0))
+                               sliding_window=c.get("W", 0), q_len=c.get("q_len", 1))
         got = pda.pda_plan_for_cus(shape, g["cu_count"])
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == \
             (c["P"], c["T_p"], c["variant"]), c["name"]
@@ -84,12 +88,15 @@ BAD_SHAPES = [
     (dict(max_seq_len=16 * 4 + 1), pda.PDA_ERR_INVALID),  # > MBS * bs
     (dict(num_blocks=0), pda.PDA_ERR_INVALID),
     (dict(sliding_window=-1), pda.PDA_ERR_INVALID),
+    (dict(q_len=-1), pda.PDA_ERR_INVALID),
+    (dict(q_len=9), pda.PDA_ERR_UNSUPPORTED),                       # 9 x 4 rows > 32
+    (dict(q_len=33, num_q_heads=8), pda.PDA_ERR_UNSUPPORTED),      # 33 rows
 ]
 
 
 def _shape(**kw):
     base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_size=128, block_size=16,
-                num_blocks=16, max_blocks_per_seq=4, max_seq_len=64, dtype=0)
+                num_blocks=16, max_blocks_per_seq=4, max_seq_len=64, dtype=0, q_len=1)
     base.update(kw)
     return pda.PdaShape(**base)
 

@@ -261,3 +261,69 @@ def test_window_covering_the_context_is_the_full_decode():
     full = oracle.decode(q, k, v, L, case.scale)
     for W in (40, 41, 1000):
         assert np.array_equal(oracle.decode(q, k, v, L, case.scale, window=W), full)
+
+
+# ---- multi-row decode: q_len causal rows per sequence ----------------------
+
+def sdpa_f64_causal(q, k, v, lens, scale, window=0):
+    """torch SDPA in float64 with an explicit [n, L] key mask: row i keeps
+    t <= L - n + i (and t > L - n + i - W with a window).  Rows whose mask is
+    empty are defined as zero (returned as such)."""
+    B, n, Hq, D = q.shape
+    out = np.zeros((B, n, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = lens[b]
+        if L == 0:
+            continue
+        t = torch.arange(L)[None, :]
+        e = (L - n + torch.arange(n) + 1)[:, None]          # exclusive end per row
+        keep = t < e
+        if window > 0:
+            keep &= t >= e - window
+        qt = torch.from_numpy(np.asarray(q[b], dtype=np.float64)).permute(1, 0, 2)[None]  # [1,Hq,n,D]
+        kt = torch.from_numpy(np.asarray(k[b], dtype=np.float64))[None]
+        vt = torch.from_numpy(np.asarray(v[b], dtype=np.float64))[None]
+        rows = keep.any(dim=1)
+        mask = keep.clone()
+        mask[~rows] = True                                   # avoid an all-masked row in SDPA
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                              scale=scale, enable_gqa=True)
+        o = o[0].permute(1, 0, 2).numpy()                    # [n, Hq, D]
+        o[~rows.numpy()] = 0.0
+        out[b] = o
+    return out
+
+
+@pytest.mark.parametrize("lens,n,W", [([40, 33], 2, 0), ([40, 33], 4, 0), ([100, 7], 8, 0),
+                                      ([3, 60], 5, 0), ([64, 48], 3, 17), ([200, 9], 4, 1),
+                                      ([37, 2], 6, 5)])
+def test_multi_row_matches_causal_sdpa(lens, n, W):
+    case = kvgen.make_case(2, 8, 2, 64, 16, lens, seed=30 + n + W, q_len=n, sliding_window=W)
+    q, k, v, L = kvgen.oracle_inputs(case)
+    got = oracle.decode_multi(q, k, v, L, case.scale, window=W)
+    ref = sdpa_f64_causal(q, k, v, L, case.scale, window=W)
+    assert got.shape == (2, n, 8, 64)
+    assert oracle.rel_linf(got, ref) <= 1e-5
+    # rows with no token (L < n) are zeros
+    for b in range(2):
+        for i in range(n):
+            if lens[b] - n + i + 1 <= 0:
+                assert np.all(got[b, i] == 0)
+
+
+def test_multi_row_last_row_is_the_plain_decode_and_one_row_is_decode():
+    n = 4
+    case = kvgen.make_case(3, 8, 4, 128, 16, [50, 17, 300], seed=41, q_len=n)
+    q, k, v, L = kvgen.oracle_inputs(case)
+    got = oracle.decode_multi(q, k, v, L, case.scale)
+    last = oracle.decode(q[:, n - 1], k, v, L, case.scale)
+    assert np.array_equal(got[:, n - 1], last)
+    # row 0 is the decode of the sequence without its last n - 1 tokens
+    k0 = [x[:, :Lb - n + 1] for x, Lb in zip(k, L)]
+    v0 = [x[:, :Lb - n + 1] for x, Lb in zip(v, L)]
+    first = oracle.decode(q[:, 0], k0, v0, [Lb - n + 1 for Lb in L], case.scale)
+    assert np.array_equal(got[:, 0], first)
+    # one row per sequence through decode_multi is decode
+    q1 = q[:, :1]
+    assert np.array_equal(oracle.decode_multi(q1, k, v, L, case.scale)[:, 0],
+                          oracle.decode(q[:, 0], k, v, L, case.scale))

@@ -18,7 +18,7 @@ def test_plan_hand_derived_values():
         g = json.load(f)
     for c in g["cases"]:
         P, T, var = plan.partition(c["B"], c["Hkv"], c["G"], c["D"], c["Lmax"], g["cu_count"],
-                                   window=c.get("W", 0))
+                                   window=c.get("W", 0), q_len=c.get("q_len", 1))
         assert (P, T, var) == (c["P"], c["T_p"], c["variant"]), c["name"]
 
 
@@ -33,9 +33,10 @@ def test_plan_invariants(D):
         L = int(rng.integers(0, 200000))
         cu = int(rng.choice([1, 80, 104, 256, 304]))
         W = int(rng.choice([0, 0, 1, 17, 1024, 4096]))
-        P, T, var = plan.partition(B, Hkv, G, D, L, cu, window=W)
-        S = plan.span(L, W)
-        assert S <= L and (W == 0 or S <= W + 15)
+        n = int(rng.choice([1, 1, 2, 4, 8]))
+        P, T, var = plan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n)
+        S = plan.span(L, W, n)
+        assert S <= L and (W == 0 or S <= W + n - 1 + 15)
         assert T % plan.TP_ALIGN == 0 and t_min <= T <= t_one
         assert P >= 1 and P * T >= S
         L = S
@@ -46,12 +47,15 @@ def test_plan_invariants(D):
             assert P * B * Hkv <= cu + B * Hkv or T == t_many
         else:
             assert P == 1
-        assert var == plan.MFMA if G > 8 else var in (plan.VALU, plan.MFMA)
+        assert var == plan.MFMA if n * G > 8 else var in (plan.VALU, plan.MFMA)
 
 
 def test_workspace_bytes():
     assert plan.workspace_bytes(1, 32, 128, 1) == 0
     assert plan.workspace_bytes(1, 24, 256, 128, 4) == 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4 + 256
+    # q_len rows per sequence: q_len times the partial rows
+    assert plan.workspace_bytes(2, 8, 64, 3, 2, q_len=4) == \
+        2 * 4 * 8 * 3 * 64 * 4 + 2 * 4 * 8 * 3 * 2 * 4 + 256
 
 
 def test_expected_trace_matches_token_loop():
@@ -83,6 +87,27 @@ def test_expected_trace_with_window_matches_token_loop():
     for b in range(3):
         L = case.seq_lens[b]
         lo = max(0, L - W)
+        base = lo - lo % 16
+        for g in range(2):
+            for t in range(64):
+                assert valid[b, g, t] == (lo <= t < L)
+                if lo <= t < L:
+                    assert slot[b, g, t] == table[b][t // 5] * 5 + t % 5
+                    assert part[b, g, t] == (t - base) // T
+            assert tuple(ranges[b, g, 0]) == (base, min(base + T, L))
+
+
+def test_expected_trace_with_window_and_rows_matches_token_loop():
+    W, n = 21, 3
+    case = kvgen.make_case(3, 8, 2, 64, 5, [0, 23, 61], seed=45, extra_blocks=2,
+                           sliding_window=W, q_len=n)
+    P, T = 1, 64
+    slot, part, ranges, valid = bookkeeping.expected_trace(
+        case.block_table.numpy(), case.seq_lens, 2, case.bs, 64, P, T, window=W, q_len=n)
+    table = case.block_table.numpy()
+    for b in range(3):
+        L = case.seq_lens[b]
+        lo = max(0, L - n + 1 - W)           # the earliest row's window
         base = lo - lo % 16
         for g in range(2):
             for t in range(64):
