@@ -175,7 +175,7 @@ def summary(name, case, r):
     kgbs = r["kv_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
     return {"workload": name, "B": case.B, "Hq": case.Hq, "Hkv": case.Hkv, "D": case.D,
             "block_size": case.bs, "dtype": case.dtype, "context_tokens": sum(case.seq_lens),
-            "sliding_window": case.sliding_window, "q_len": case.q_len,
+            "sliding_window": case.sliding_window, "q_len": case.q_len, "kv_dtype": case.kv_dtype,
             "kv_bytes": r["kv_bytes"], "P": r["plan"].num_partitions,
             "T_p": r["plan"].tokens_per_partition, "us_per_call": round(us, 3),
             "splitkv_kernel_us": round(kus, 3), "GBps": round(gbs, 1),
@@ -297,6 +297,10 @@ def main():
         specs += [(f"cfg3 sliding W1024 B{b} 32K", lambda b=b: configs.cfg3_sliding(b, L, device="cuda"))
                   for b in (1, 8)]
         specs += [("cfg4 TP2 share 12/2 32K", lambda: configs.cfg4_tp2(L, device="cuda"))]
+        specs += [("headline fp8 KV 32K", lambda: configs.cfg2(32, L, device="cuda", kv_dtype="fp8")),
+                  ("cfg3 B8 fp8 KV 32K", lambda: configs.cfg3(8, L, device="cuda", kv_dtype="fp8")),
+                  ("cfg4 fp8 KV 32K", lambda: configs.cfg4(L, device="cuda", kv_dtype="fp8")),
+                  ("cfg5 B64 mixed fp8 KV", lambda: configs.cfg5(device="cuda", kv_dtype="fp8"))]
         specs += [("headline q_len 4 32K", lambda: configs.cfg2(32, L, device="cuda", q_len=4)),
                   ("cfg3 B8 q_len 4 32K", lambda: configs.cfg3(8, L, device="cuda", q_len=4)),
                   ("cfg5 B64 mixed q_len 2", lambda: configs.cfg5(device="cuda", q_len=2))]

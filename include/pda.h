@@ -54,6 +54,17 @@
  * the kernels read every K/V byte once for all R rows.  A row whose range is
  * empty (L < n) yields zeros.
  *
+ * fp8 KV cache (pda_shape_t.kv_dtype = PDA_KV_FP8_E4M3): k_cache and v_cache
+ * hold one byte per element in the OCP FP8 E4M3 format (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; subnormals; no infinity; S.1111.111 is
+ * NaN; largest finite 448), with one scale per tensor: the element's value is
+ * decode(byte) * k_scale (resp. v_scale).  This halves the KV bytes per token
+ * (the fp8 KV the first page lists as untested, section 6).  q and out keep
+ * the 16-bit type of `dtype`.  The kernels decode the bytes exactly (every
+ * E4M3 value is a 16-bit and an fp32 value), fold k_scale into the score
+ * scale and v_scale into the output; arithmetic is the same fp32 as for
+ * 16-bit KV.  Only the MFMA variant serves fp8 KV.
+ *
  * Device-data contract (not checked on the hot path; violating it is
  * undefined behaviour):
  *  - 0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size;
@@ -81,10 +92,14 @@ extern "C" {
 #define PDA_ERR_DEVICE       -5  /* the HIP device query failed */
 
 /* ---- element types ----------------------------------------------------- */
-/* q, k_cache, v_cache and out share one 16-bit type; arithmetic is fp32 and
- * the output is rounded to nearest-even. */
+/* q and out share one 16-bit type (dtype); k_cache and v_cache have it too
+ * (kv_dtype PDA_KV_SAME) or are fp8 E4M3 bytes with per-tensor scales
+ * (kv_dtype PDA_KV_FP8_E4M3).  Arithmetic is fp32 and the output is rounded
+ * to nearest-even. */
 #define PDA_BF16 0
 #define PDA_FP16 1
+#define PDA_KV_SAME      0
+#define PDA_KV_FP8_E4M3  1
 
 /* Largest supported query-to-KV head ratio G, and largest number of rows
  * R = q_len * G one unit packs (two 16-row matrix-core tiles). */
@@ -112,13 +127,13 @@ extern "C" {
  * sliding window W > 0 (the union of the rows' windows, rounded out to the
  * 16-token grid the partitions start on):
  *
- * Variant: MFMA if R > PDA_VALU_MAX_GROUP, or if R >= PDA_MFMA_MIN_GROUP and
- *   B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU load of the matrix cores
- *   pays); VALU otherwise (one row per unit, where the VALU kernel has
- *   the least to do, or many units over many rounds, where its higher
- *   occupancy pays).
- * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D (K and V bytes per
- *   token of one KV head):
+ * Variant: MFMA for fp8 KV, if R > PDA_VALU_MAX_GROUP, or if R >=
+ *   PDA_MFMA_MIN_GROUP and B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU
+ *   load of the matrix cores pays); VALU otherwise (one row per unit, where
+ *   the VALU kernel has the least to do, or many units over many rounds,
+ *   where its higher occupancy pays).
+ * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D, or 2*D for fp8 KV
+ *   (K and V bytes per token of one KV head):
  *   T_min  = max(ALIGN, floor(PDA_WG_MIN_BYTES  / bpt / ALIGN) * ALIGN)
  *   T_many = max(T_min, floor(PDA_WG_MANY_BYTES / bpt / ALIGN) * ALIGN)
  *   T_one  = max(T_many, floor(PDA_WG_ONE_BYTES / bpt / ALIGN) * ALIGN)
@@ -176,6 +191,8 @@ typedef struct pda_shape {
     int32_t dtype;               /* PDA_BF16 or PDA_FP16 */
     int32_t sliding_window;      /* W >= 0; 0: attend to the whole context (see above) */
     int32_t q_len;               /* query rows per sequence, 1..; 0 is read as 1 (see above) */
+    int32_t kv_dtype;            /* PDA_KV_SAME or PDA_KV_FP8_E4M3 (see above) */
+    float k_scale, v_scale;      /* fp8 KV: per-tensor scales, finite and > 0; else unused */
 } pda_shape_t;
 
 typedef struct pda_plan {
@@ -212,8 +229,8 @@ int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* strea
 
 /* The decode step, under the device's own plan.
  *   q            [B][q_len][Hq][D]    16-bit, the query rows of each sequence
- *   k_cache      [NB][Hkv][bs][D]     16-bit, the paged K pool
- *   v_cache      [NB][Hkv][bs][D]     16-bit, the paged V pool (same layout)
+ *   k_cache      [NB][Hkv][bs][D]     16-bit or fp8 (kv_dtype), the paged K pool
+ *   v_cache      [NB][Hkv][bs][D]     the paged V pool (same type and layout)
  *   block_table  [B][MBS]             int32 physical block ids, row-major
  *   seq_lens     [B]                  int32 context lengths
  *   scale        multiplies q.k before the softmax (usually 1/sqrt(D))

@@ -40,6 +40,10 @@ def cdiv(a: int, b: int) -> int:
 
 _DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
 _TAIL = {"zero": 0.0, "nan": float("nan"), "1e4": 1.0e4}
+# the same fills as OCP E4M3 bytes (fp8 KV): zero, NaN (S.1111.111), and
+# the largest finite value 448 standing in for a large finite garbage value
+_TAIL_FP8 = {"zero": 0x00, "nan": 0x7F, "1e4": 0x7E}
+FP8_MAX = 448.0
 
 
 @dataclass
@@ -67,6 +71,9 @@ class Case:
     tail_v: str = "zero"
     sliding_window: int = 0         # W > 0: decode attends to the last W tokens
     q_len: int = 1                  # query rows per sequence (causal among themselves)
+    kv_dtype: str = "same"          # "fp8": k, v and the pools hold E4M3 bytes (float8_e4m3fn)
+    k_scale: float = 1.0            # fp8: value = decode(byte) * scale, per tensor
+    v_scale: float = 1.0
 
     @property
     def G(self) -> int:
@@ -81,8 +88,10 @@ class Case:
         return L
 
     def kv_bytes(self) -> int:
-        """Algorithmic KV bytes: attended tokens only, K and V, 16-bit."""
-        return sum(self.attended(b) for b in range(self.B)) * self.Hkv * self.D * 2 * 2
+        """Algorithmic KV bytes: attended tokens only, K and V, 2 bytes per
+        element (1 for fp8 KV)."""
+        eb = 1 if self.kv_dtype == "fp8" else 2
+        return sum(self.attended(b) for b in range(self.B)) * self.Hkv * self.D * 2 * eb
 
 
 def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int],
@@ -90,7 +99,7 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
               max_blocks_per_seq: Optional[int] = None, tail_k: str = "zero",
               tail_v: str = "zero", scale: Optional[float] = None,
               max_seq_len: Optional[int] = None, sliding_window: int = 0,
-              q_len: int = 1) -> Case:
+              q_len: int = 1, kv_dtype: str = "same") -> Case:
     assert len(seq_lens) == B and Hq % Hkv == 0
     tdt = _DT[dtype]
     device = torch.device(device)
@@ -101,8 +110,20 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
     q = torch.randn(qshape, generator=gen, device=device).to(tdt)
     k, v = [], []
     for b in range(B):
-        k.append(torch.randn((Hkv, lens[b], D), generator=gen, device=device).to(tdt))
-        v.append(torch.randn((Hkv, lens[b], D), generator=gen, device=device).to(tdt))
+        k.append(torch.randn((Hkv, lens[b], D), generator=gen, device=device))
+        v.append(torch.randn((Hkv, lens[b], D), generator=gen, device=device))
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8":
+        # per-tensor scales that map the largest |value| to the largest E4M3
+        # value, then round to E4M3 (nearest even; within range by construction)
+        def amax(xs):
+            return max([float(x.abs().max()) for x in xs if x.numel()] + [1e-30])
+        k_scale, v_scale = amax(k) / FP8_MAX, amax(v) / FP8_MAX
+        k = [(x / k_scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn) for x in k]
+        v = [(x / v_scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn) for x in v]
+    else:
+        k = [x.to(tdt) for x in k]
+        v = [x.to(tdt) for x in v]
     nbs = [cdiv(L, bs) for L in lens]
     used = sum(nbs)
     NB = used + max(1, int(extra_blocks))
@@ -122,7 +143,8 @@ def make_case(B: int, Hq: int, Hkv: int, D: int, bs: int, seq_lens: Sequence[int
                 num_blocks=NB, max_blocks_per_seq=MBS,
                 max_seq_len=int(max_seq_len) if max_seq_len is not None else max(lens),
                 unref_ids=unref, tail_k=tail_k, tail_v=tail_v,
-                sliding_window=int(sliding_window), q_len=int(q_len))
+                sliding_window=int(sliding_window), q_len=int(q_len), kv_dtype=kv_dtype,
+                k_scale=float(k_scale), v_scale=float(v_scale))
     return page(case, tail_k=tail_k, tail_v=tail_v)
 
 
@@ -134,10 +156,12 @@ def page(case: Case, tail_k: str = "zero", tail_v: str = "zero",
     table = case.block_table if block_table is None else block_table
     unref = case.unref_ids if unref_ids is None else unref_ids
     dev = case.q.device
-    tdt = case.q.dtype
+    fp8 = case.kv_dtype == "fp8"
+    tdt = torch.uint8 if fp8 else case.q.dtype     # fp8 pools are built as their bytes
+    fills = _TAIL_FP8 if fp8 else _TAIL
     shape = (case.num_blocks, case.Hkv, case.bs, case.D)
-    kc = torch.full(shape, _TAIL[tail_k], dtype=tdt, device=dev)
-    vc = torch.full(shape, _TAIL[tail_v], dtype=tdt, device=dev)
+    kc = torch.full(shape, fills[tail_k], dtype=tdt, device=dev)
+    vc = torch.full(shape, fills[tail_v], dtype=tdt, device=dev)
     tcpu = table.cpu()
     for b in range(case.B):
         L = case.seq_lens[b]
@@ -146,9 +170,11 @@ def page(case: Case, tail_k: str = "zero", tail_v: str = "zero",
             continue
         ids = tcpu[b, :nb].to(torch.int64).to(dev)
         for src, dst, fill in ((case.k[b], kc, tail_k), (case.v[b], vc, tail_v)):
-            padded = torch.full((case.Hkv, nb * case.bs, case.D), _TAIL[fill], dtype=tdt, device=dev)
-            padded[:, :L] = src
+            padded = torch.full((case.Hkv, nb * case.bs, case.D), fills[fill], dtype=tdt, device=dev)
+            padded[:, :L] = src.view(torch.uint8) if fp8 else src
             dst[ids] = padded.view(case.Hkv, nb, case.bs, case.D).permute(1, 0, 2, 3)
+    if fp8:
+        kc, vc = kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn)
     return replace(case, k_cache=kc, v_cache=vc, block_table=table.to(dev),
                    unref_ids=list(unref), tail_k=tail_k, tail_v=tail_v)
 
@@ -176,7 +202,11 @@ def poison_before_window(case: Case, fill: str = "nan") -> Case:
     sliding window (t < L_b - q_len + 1 - W, before the window of its earliest
     query row) overwritten with `fill`: tokens the decode must not read."""
     assert case.sliding_window > 0
+    fp8 = case.kv_dtype == "fp8"
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    if fp8:
+        kc, vc = kc.view(torch.uint8), vc.view(torch.uint8)
+    value = _TAIL_FP8[fill] if fp8 else _TAIL[fill]
     table = case.block_table.cpu().to(torch.int64)
     for b in range(case.B):
         lo = max(0, case.seq_lens[b] - case.q_len + 1 - case.sliding_window)
@@ -186,16 +216,25 @@ def poison_before_window(case: Case, fill: str = "nan") -> Case:
         blocks = table[b, t // case.bs].to(kc.device)
         slots = (t % case.bs).to(kc.device)
         for h in range(case.Hkv):
-            kc[blocks, h, slots] = _TAIL[fill]
-            vc[blocks, h, slots] = _TAIL[fill]
+            kc[blocks, h, slots] = value
+            vc[blocks, h, slots] = value
+    if fp8:
+        kc, vc = kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn)
     return replace(case, k_cache=kc, v_cache=vc)
 
 
 def oracle_inputs(case: Case, seqs: Optional[Sequence[int]] = None):
-    """fp32 numpy inputs for the oracle (exact upcasts), optionally for a
-    subset of sequences (re-indexed 0..len(seqs)-1)."""
+    """Numpy inputs for the oracle, optionally for a subset of sequences
+    (re-indexed 0..len(seqs)-1): q as fp32 (an exact upcast); K and V as fp32
+    exact upcasts, or for fp8 KV as their E4M3 bytes (uint8), which the
+    oracle decodes with case.k_scale / case.v_scale."""
     idx = list(range(case.B)) if seqs is None else list(seqs)
     q = case.q[idx].float().cpu().numpy()
+    if case.kv_dtype == "fp8":
+        k = [case.k[b].view(torch.uint8).cpu().numpy() for b in idx]
+        v = [case.v[b].view(torch.uint8).cpu().numpy() for b in idx]
+        lens = [case.seq_lens[b] for b in idx]
+        return q, k, v, lens
     k = [case.k[b].float().cpu().numpy() for b in idx]
     v = [case.v[b].float().cpu().numpy() for b in idx]
     lens = [case.seq_lens[b] for b in idx]
@@ -206,4 +245,5 @@ def shape_dict(case: Case) -> dict:
     return dict(num_seqs=case.B, num_q_heads=case.Hq, num_kv_heads=case.Hkv,
                 head_size=case.D, block_size=case.bs, num_blocks=case.num_blocks,
                 max_blocks_per_seq=case.max_blocks_per_seq, max_seq_len=case.max_seq_len,
-                dtype=case.dtype, sliding_window=case.sliding_window, q_len=case.q_len)
+                dtype=case.dtype, sliding_window=case.sliding_window, q_len=case.q_len,
+                kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)

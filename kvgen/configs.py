@@ -22,7 +22,9 @@
         TP=2: page "vLLM's custom ROCm paged-attention kernel wins all sixty
         cells", section 4); same shapes otherwise.
 Every shape takes q_len > 1 for multi-row decode (that many query rows at
-the end of each sequence, causal among themselves).
+the end of each sequence, causal among themselves) and kv_dtype="fp8" for an
+OCP E4M3 KV cache (K and V drawn as above, then rounded to E4M3 under one
+scale per tensor that maps the largest |value| to 448).
 Lengths "1K..32K" are read as powers of two, 1024..32768; "16k+1" and "16k+7"
 as 16385 and 16391.
 """
@@ -43,16 +45,17 @@ def cfg1(dtype: str = "bf16", device="cpu", tail: str = "nan") -> Case:
 
 
 def cfg2(hq: int, L: int, device="cpu", dtype: str = "bf16", cell: int = 0,
-         q_len: int = 1) -> Case:
+         q_len: int = 1, kv_dtype: str = "same") -> Case:
     return make_case(B=1, Hq=hq, Hkv=8, D=128, bs=16, seq_lens=[L], dtype=dtype,
-                     seed=seed_for(2, cell), device=device, extra_blocks=1, q_len=q_len)
+                     seed=seed_for(2, cell), device=device, extra_blocks=1, q_len=q_len,
+                     kv_dtype=kv_dtype)
 
 
 def cfg3(B: int, L: int, dtype: str = "bf16", device="cpu", tail_k: str = "nan",
-         tail_v: str = "nan", cell: int = 0, q_len: int = 1) -> Case:
+         tail_v: str = "nan", cell: int = 0, q_len: int = 1, kv_dtype: str = "same") -> Case:
     return make_case(B=B, Hq=32, Hkv=16, D=128, bs=16, seq_lens=[L] * B, dtype=dtype,
                      seed=seed_for(3, cell), device=device, extra_blocks=1,
-                     tail_k=tail_k, tail_v=tail_v, q_len=q_len)
+                     tail_k=tail_k, tail_v=tail_v, q_len=q_len, kv_dtype=kv_dtype)
 
 
 def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu",
@@ -63,10 +66,10 @@ def cfg3_sliding(B: int, L: int, W: int = 1024, dtype: str = "bf16", device="cpu
 
 
 def cfg4(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0,
-         q_len: int = 1) -> Case:
+         q_len: int = 1, kv_dtype: str = "same") -> Case:
     return make_case(B=1, Hq=24, Hkv=4, D=256, bs=784, seq_lens=[L], dtype=dtype,
                      seed=seed_for(4, cell), device=device, extra_blocks=1,
-                     tail_k=tail, tail_v=tail, q_len=q_len)
+                     tail_k=tail, tail_v=tail, q_len=q_len, kv_dtype=kv_dtype)
 
 
 def cfg4_tp2(L: int, device="cpu", dtype: str = "bf16", tail: str = "nan", cell: int = 0) -> Case:
@@ -94,8 +97,9 @@ def cfg5_lens(seed: int, B: int = 64, lo: int = 1024, hi: int = 32768):
 
 
 def cfg5(device="cpu", dtype: str = "bf16", B: int = 64, lo: int = 1024, hi: int = 32768,
-         cell: int = 0, q_len: int = 1) -> Case:
+         cell: int = 0, q_len: int = 1, kv_dtype: str = "same") -> Case:
     seed = seed_for(5, cell)
     lens = cfg5_lens(seed + 1, B=B, lo=lo, hi=hi)
     return make_case(B=B, Hq=32, Hkv=8, D=128, bs=16, seq_lens=lens, dtype=dtype, seed=seed,
-                     device=device, extra_blocks=1, tail_k="nan", tail_v="nan", q_len=q_len)
+                     device=device, extra_blocks=1, tail_k="nan", tail_v="nan", q_len=q_len,
+                     kv_dtype=kv_dtype)

@@ -28,6 +28,12 @@ Contents
   bookkeeping                      expected per-token physical slot and
                                    partition, and per-unit token ranges
                                    (bookkeeping.py).
+  e4m3_value / dequantize_e4m3     the OCP FP8 E4M3 code -> value map, from
+                                   the format's definition, and per-tensor
+                                   dequantisation (fp8 KV: the fp8 KV the
+                                   first page lists as untested, section 6);
+                                   decode* take kv_scales=(k_scale, v_scale)
+                                   to read K/V given as E4M3 bytes.
   rel_linf                         the pages' score: relative L-infinity
                                    against the reference's own scale.
 
@@ -105,6 +111,32 @@ class _Packed:
             self.v[o:o + n] = np.asarray(v[b], dtype=np.float32).reshape(-1)
 
 
+def e4m3_value(codes) -> np.ndarray:
+    """Values (float64) of OCP FP8 E4M3 bytes, from the format's definition:
+    bit 7 the sign, bits 6-3 the exponent e with bias 7, bits 2-0 the
+    mantissa m; e == 0 is subnormal, m/8 * 2^-6; otherwise (1 + m/8) * 2^(e-7);
+    e == 15 with m == 7 is NaN; there is no infinity (largest value 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    val = np.where(c & 0x80, -mag, mag)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+
+
+def dequantize_e4m3(codes, scale: float) -> np.ndarray:
+    """float32 values of E4M3 bytes under a per-tensor scale: value * scale
+    (one rounding to fp32)."""
+    return (e4m3_value(codes) * float(scale)).astype(np.float32)
+
+
+def _kv_values(k, v, kv_scales):
+    if kv_scales is None:
+        return k, v
+    ks, vs = kv_scales
+    return ([dequantize_e4m3(x, ks) for x in k], [dequantize_e4m3(x, vs) for x in v])
+
+
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
@@ -123,9 +155,12 @@ def _window(k, v, seq_lens, window: int):
     return k, v, [lens[b] - lo[b] for b in range(len(lens))]
 
 
-def decode(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.ndarray:
-    """All rows: float32 [B, Hq, D]."""
+def decode(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0,
+           kv_scales=None) -> np.ndarray:
+    """All rows: float32 [B, Hq, D].  kv_scales=(k_scale, v_scale): k and v
+    are E4M3 bytes, dequantised first."""
     lib = _load()
+    k, v = _kv_values(k, v, kv_scales)
     k, v, seq_lens = _window(k, v, seq_lens, window)
     pk = _Packed(q, k, v, seq_lens)
     out = np.empty((pk.B, pk.Hq, pk.D), dtype=np.float32)
@@ -137,7 +172,8 @@ def decode(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.n
     return out
 
 
-def decode_multi(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -> np.ndarray:
+def decode_multi(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0,
+                 kv_scales=None) -> np.ndarray:
     """q float32 [B, n, Hq, D]: n query rows per sequence, row i at position
     L - n + i.  Row i attends to the tokens t <= L - n + i (causal among the
     new rows, whose K/V are the sequence's last n), and with a sliding window
@@ -146,6 +182,7 @@ def decode_multi(q, k, v, seq_lens, scale, nthreads: int = 0, window: int = 0) -
     not positive).  Returns float32 [B, n, Hq, D]."""
     q = np.asarray(q, dtype=np.float32)
     B, n, Hq, D = q.shape
+    k, v = _kv_values(k, v, kv_scales)
     kk, vv, ll = [], [], []
     for b in range(B):
         L = int(seq_lens[b])

@@ -26,19 +26,20 @@ def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def variant(num_seqs: int, num_kv_heads: int, group: int, q_len: int = 1) -> int:
-    """MFMA above the VALU row limit, or for R = q_len * G >= 2 rows with at
-    most 128 units."""
+def variant(num_seqs: int, num_kv_heads: int, group: int, q_len: int = 1,
+            kv_fp8: bool = False) -> int:
+    """MFMA for fp8 KV, above the VALU row limit, or for R = q_len * G >= 2
+    rows with at most 128 units."""
     units = num_seqs * num_kv_heads
     rows = max(1, q_len) * group
-    if rows > VALU_MAX_GROUP or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
+    if kv_fp8 or rows > VALU_MAX_GROUP or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
         return MFMA
     return VALU
 
 
-def token_bounds(head_size: int):
+def token_bounds(head_size: int, kv_fp8: bool = False):
     """(T_min, T_many, T_one) in tokens."""
-    bpt = 4 * head_size  # K and V, 16-bit, one KV head
+    bpt = (2 if kv_fp8 else 4) * head_size  # K and V bytes of one token and KV head
     t_min = max(TP_ALIGN, (WG_MIN_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
     t_many = max(t_min, (WG_MANY_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
     t_one = max(t_many, (WG_ONE_BYTES // bpt // TP_ALIGN) * TP_ALIGN)
@@ -54,10 +55,10 @@ def span(max_seq_len: int, window: int = 0, q_len: int = 1) -> int:
 
 
 def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_seq_len: int,
-              cu_count: int, window: int = 0, q_len: int = 1):
+              cu_count: int, window: int = 0, q_len: int = 1, kv_fp8: bool = False):
     """(P, T_p, variant) for the documented rule."""
-    var = variant(num_seqs, num_kv_heads, group, q_len)
-    t_min, t_many, t_one = token_bounds(head_size)
+    var = variant(num_seqs, num_kv_heads, group, q_len, kv_fp8)
+    t_min, t_many, t_one = token_bounds(head_size, kv_fp8)
     units = num_seqs * num_kv_heads
     p_fill = _cdiv(cu_count, units)
     lspan = span(max_seq_len, window, q_len)

@@ -27,12 +27,15 @@ PDA_ERR_LAUNCH = -4
 PDA_ERR_DEVICE = -5
 PDA_BF16 = 0
 PDA_FP16 = 1
+PDA_KV_SAME = 0
+PDA_KV_FP8_E4M3 = 1
 PDA_VARIANT_VALU = 1
 PDA_VARIANT_MFMA = 2
 PDA_MERGE_FUSED = 0
 PDA_MERGE_KERNEL = 1
 
 _DTYPES = {"bf16": PDA_BF16, "fp16": PDA_FP16}
+_KV_DTYPES = {"same": PDA_KV_SAME, "fp8": PDA_KV_FP8_E4M3, "fp8_e4m3": PDA_KV_FP8_E4M3}
 
 
 class PdaShape(ctypes.Structure):
@@ -41,7 +44,8 @@ class PdaShape(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("sliding_window", ctypes.c_int32),
-                ("q_len", ctypes.c_int32)]
+                ("q_len", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class PdaPlan(ctypes.Structure):
@@ -105,18 +109,23 @@ def load_library():
 
 def make_shape(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_blocks,
                max_blocks_per_seq, max_seq_len, dtype="bf16", sliding_window=0,
-               q_len=1) -> PdaShape:
+               q_len=1, kv_dtype="same", k_scale=1.0, v_scale=1.0) -> PdaShape:
     """sliding_window W > 0: attend to the last W tokens of each sequence.
-    q_len > 1: that many query rows per sequence, causal among themselves."""
+    q_len > 1: that many query rows per sequence, causal among themselves.
+    kv_dtype "fp8": the caches hold OCP E4M3 bytes, value = byte * k_scale /
+    v_scale."""
     dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    kvt = _KV_DTYPES[kv_dtype] if isinstance(kv_dtype, str) else int(kv_dtype)
     return PdaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_size),
                     int(block_size), int(num_blocks), int(max_blocks_per_seq), int(max_seq_len),
-                    dt, int(sliding_window), int(q_len))
+                    dt, int(sliding_window), int(q_len), kvt, float(k_scale), float(v_scale))
 
 
 def shape_from_tensors(q, k_cache, block_table, max_seq_len: int,
-                       sliding_window: int = 0) -> PdaShape:
-    """q is [B, Hq, D] (one query row per sequence) or [B, q_len, Hq, D]."""
+                       sliding_window: int = 0, k_scale: float = 1.0,
+                       v_scale: float = 1.0) -> PdaShape:
+    """q is [B, Hq, D] (one query row per sequence) or [B, q_len, Hq, D];
+    k_cache of q's dtype, or float8_e4m3fn with per-tensor scales."""
     import torch
     if q.dim() == 3:
         B, Hq, D = q.shape
@@ -131,8 +140,9 @@ def shape_from_tensors(q, k_cache, block_table, max_seq_len: int,
     dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(q.dtype)
     if dt is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    kvt = "fp8" if k_cache.dtype == torch.float8_e4m3fn else "same"
     return make_shape(B, Hq, Hkv, D, bs, NB, block_table.shape[1], max_seq_len, dt,
-                      sliding_window, q_len)
+                      sliding_window, q_len, kvt, k_scale, v_scale)
 
 
 def pda_status_string(status: int) -> str:
@@ -195,8 +205,10 @@ def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
             raise ValueError(f"{name} must be contiguous")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
-    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype):
-        raise ValueError("q, k_cache, v_cache and out must share one dtype")
+    if q.dtype != out.dtype or k_cache.dtype != v_cache.dtype:
+        raise ValueError("q and out, and k_cache and v_cache, must share one dtype")
+    if k_cache.dtype not in (q.dtype, torch.float8_e4m3fn):
+        raise ValueError("k_cache/v_cache must have q's dtype or be float8_e4m3fn")
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must have the same shape")
     if out.shape != q.shape:
@@ -207,12 +219,14 @@ def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
 
 def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, out=None,
                       workspace=None, max_seq_len: Optional[int] = None, plan: Optional[PdaPlan] = None,
-                      stream=None, sliding_window: int = 0):
+                      stream=None, sliding_window: int = 0, k_scale: float = 1.0,
+                      v_scale: float = 1.0):
     """Decode the query rows of each sequence over the paged KV cache.
 
     q [B, Hq, D] (one row per sequence) or [B, q_len, Hq, D] (q_len rows at
     the sequence's last q_len positions, causal among themselves),
-    k_cache/v_cache [NB, Hkv, bs, D] (bf16 or fp16, one dtype),
+    k_cache/v_cache [NB, Hkv, bs, D] (q's bf16/fp16 dtype, or float8_e4m3fn
+    with per-tensor scales k_scale / v_scale),
     block_table [B, MBS] int32, seq_lens [B] int32, all on the current device.
     max_seq_len must bound every seq_lens entry (default: block_table width *
     block size, which is always valid but may over-partition).
@@ -224,7 +238,8 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
     _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out)
     if max_seq_len is None:
         max_seq_len = block_table.shape[1] * k_cache.shape[2]
-    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window)
+    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window, k_scale,
+                               v_scale)
     lib = load_library()
     if plan is None:
         need = paged_decode_attn_workspace_size(shape)
@@ -250,10 +265,12 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
 def paged_decode_attn_with_plan(q, k_cache, v_cache, block_table, seq_lens, scale: float,
                                 plan: PdaPlan, out=None, workspace=None,
                                 max_seq_len: Optional[int] = None, stream=None,
-                                sliding_window: int = 0):
+                                sliding_window: int = 0, k_scale: float = 1.0,
+                                v_scale: float = 1.0):
     return paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale, out=out,
                              workspace=workspace, max_seq_len=max_seq_len, plan=plan,
-                             stream=stream, sliding_window=sliding_window)
+                             stream=stream, sliding_window=sliding_window, k_scale=k_scale,
+                             v_scale=v_scale)
 
 
 def paged_decode_attn_workspace_init(workspace, stream=None):

@@ -1,8 +1,9 @@
 """Build libpda.so in-tree with hipcc for gfx950 only.
 
 Every translation unit is compiled in parallel into _build/, then linked into
-paged_kv_cache_decode_amd/libpda.so.  The decode kernel's source is compiled
-once per (element type, head size).
+paged_kv_cache_decode_amd/libpda.so.  The decode kernels' sources are compiled
+once per (element type, head size), the matrix-core one also per KV type
+(16-bit or fp8).
 """
 import os
 import subprocess
@@ -32,6 +33,8 @@ def _units(csrc=CSRC):
                           f"valu_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
             units.append((os.path.join(csrc, "pda_decode_mfma.hip"),
                           f"mfma_{dt}_{hd}.o", [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}"]))
+            units.append((os.path.join(csrc, "pda_decode_mfma.hip"), f"mfma8_{dt}_{hd}.o",
+                          [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}", "-DPDA_KV_FP8=1"]))
     units.append((os.path.join(csrc, "pda_merge.hip"), "merge.o", []))
     units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
     flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops"])

@@ -25,9 +25,19 @@
 // VALU work per tile is reduced to the 16-bit -> fp32 conversion of V and the
 // softmax bookkeeping, independent of the row count.
 //
-// Compiled once per (element type, head size): PDA_DTYPE (0 bf16, 1 fp16)
-// and PDA_HEAD (64, 128, 256).
+// fp8 KV (F8): K and V rows are OCP E4M3 bytes.  A lane's 16-byte K load
+// then holds 16 elements, d = 64*s2 + 16*q4 .. +16, decoded exactly to the
+// 16-bit type as the A operands of k-steps 2*s2 and 2*s2 + 1; the query
+// elements of each k-step are loaded in the same permuted order of d (a dot
+// product does not depend on the order of its terms).  V chunks are 8-byte
+// loads decoded to fp32.  k_scale is folded into the score scale and v_scale
+// into the output (write_unit_rows).
+//
+// Compiled once per (element type, head size, KV type): PDA_DTYPE (0 bf16,
+// 1 fp16), PDA_HEAD (64, 128, 256) and PDA_KV_FP8 (0: 16-bit KV, 1: fp8).
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "pda_device.h"
 
@@ -36,6 +46,16 @@
 #endif
 #ifndef PDA_HEAD
 #error "PDA_HEAD must be defined"
+#endif
+#ifndef PDA_KV_FP8
+#define PDA_KV_FP8 0
+#endif
+// Register-buffer stages of the tile pipeline, chosen by measurement
+#ifndef PDA_MFMA_STAGES
+#define PDA_MFMA_STAGES 2
+#endif
+#ifndef PDA_MFMA_STAGES_FP8
+#define PDA_MFMA_STAGES_FP8 2
 #endif
 
 namespace pda {
@@ -93,11 +113,17 @@ __device__ inline float sum_token_groups(float x) {
 // 4 columns of d, rows = the 4 rows of a block; no padding to 16, a quarter
 // of the matrix-core cycles per block.  Each lane group (l / 16) accumulates
 // over its own tokens; the four partial sums are added once at the end.
-template <typename Elt, int D, bool ALIGNED, bool BUF, int NG, int RC>
+template <typename Elt, int D, bool ALIGNED, bool BUF, int NG, int RC, bool F8>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(RC == 1 || (RC == 2 && NG == 0), "two row chunks use the padded PV form");
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
+    constexpr int EB = F8 ? 1 : 2;             // KV bytes per element
+    // tiles in register buffers (fp8 tiles are half the bytes and registers)
+    constexpr int S = F8 ? PDA_MFMA_STAGES_FP8 : PDA_MFMA_STAGES;
+    static_assert(S >= 2 && S <= 6, "stages");
+    constexpr int KL = F8 ? KS / 2 : KS;       // 16-byte K loads per lane and tile
+    using VRaw = typename std::conditional<F8, uint2, uint4>::type;  // 8 V elements
     extern __shared__ float smem[];
     float* red = smem;                                                       // [kWaves][8][D+2]
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * kHeadChunk * (D + 2));
@@ -121,10 +147,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int c = 0; c < RC; ++c) {
         lrow[c] = min(16 * c + c16, R - 1);
-        const uint16_t* qrow =
-            static_cast<const uint16_t*>(p.q) + row_index(p, b, g, lrow[c]) * D + 8 * q4;
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + row_index(p, b, g, lrow[c]) * D;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qb[c][s] = *reinterpret_cast<const uint4*>(qrow + 32 * s);
+        for (int s = 0; s < KS; ++s) {
+            // elements of k-step s in the lane's K operand (see the file comment)
+            const int e0 = F8 ? 64 * (s / 2) + 16 * q4 + 8 * (s % 2) : 32 * s + 8 * q4;
+            qb[c][s] = *reinterpret_cast<const uint4*>(qrow + e0);
+        }
     }
     const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
     TileBlock first[2] = {{0, 0}, {0, 0}};
@@ -161,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const char* kc = static_cast<const char*>(p.k_cache);
     const char* vc = static_cast<const char*>(p.v_cache);
     const int64_t head_off = (int64_t)g * p.head_stride;               // elements
-    const uint32_t k_lane = (uint32_t)(8 * q4) * 2;                     // bytes
-    const uint32_t v_lane = (uint32_t)(8 * (c16 % CW)) * 2;             // bytes
+    const uint32_t k_lane = (uint32_t)(16 * q4);                        // bytes
+    const uint32_t v_lane = (uint32_t)(8 * (c16 % CW)) * EB;            // bytes
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
     // Tile jj >= ntiles is a prefetch past the end: with buffer loads (BUF)
@@ -182,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             first[1] = tile_block(p, trow, tile_start(wave + kWaves));
     }
     // `tb` is the tile's block on the aligned path (tile_block of tile_start)
-    auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[KS], uint4 (&vr)[4][DH]) {
+    auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[KL], VRaw (&vr)[4][DH]) {
         const bool valid = jj < ntiles;
         const int tile_base = tile_start(jj);
         int phys = tb.phys, slot0 = tb.slot0, dt;
@@ -193,10 +222,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                               dt);
         }
         {
-            const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
-            const uint32_t off = (uint32_t)dt * (2 * D) + k_lane;
+            const int64_t base =
+                EB * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+            const uint32_t off = (uint32_t)dt * (EB * D) + k_lane;
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KL; ++s)
                 kr[s] = kBuf ? load_row16_buf(kc + base, off + 64 * s, valid)
                              : load_row16(kc + base + off + 64 * s);
         }
@@ -208,12 +238,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, mfma_v_offset(lane, r), phys,
                                   slot0, dt);
             }
-            const int64_t base = 2 * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
-            const uint32_t off = (uint32_t)dt * (2 * D) + v_lane;
+            const int64_t base =
+                EB * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+            const uint32_t off = (uint32_t)dt * (EB * D) + v_lane;
 #pragma unroll
-            for (int dh = 0; dh < DH; ++dh)
-                vr[r][dh] = kBuf ? load_row16_buf(vc + base, off + 256 * dh, valid)
-                                 : load_row16(vc + base + off + 256 * dh);
+            for (int dh = 0; dh < DH; ++dh) {
+                if constexpr (F8)
+                    vr[r][dh] = kBuf ? load_row8_buf(vc + base, off + 128 * dh, valid)
+                                     : load_row8(vc + base + off + 128 * dh);
+                else
+                    vr[r][dh] = kBuf ? load_row16_buf(vc + base, off + 256 * dh, valid)
+                                     : load_row16(vc + base + off + 256 * dh);
+            }
         }
     };
     auto block_of = [&](int jj) {
@@ -238,15 +274,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         l[c] = 0.f;       // this lane's share of that row's denominator
     }
 
-    auto process = [&](int j, const uint4 (&kr)[KS], const uint4 (&vr)[4][DH]) {
+    auto process = [&](int j, const uint4 (&kr)[KL], const VRaw (&vr)[4][DH]) {
         const int tile_base = t0 + j * TT;
         const bool full = full_tile(rg, tile_base, TT, t1);
+        // the A operands of the k-steps (fp8 bytes decoded to the 16-bit type)
+        uint4 ka[KS];
+#pragma unroll
+        for (int s = 0; s < KL; ++s) {
+            if constexpr (F8) {
+                ka[2 * s] = fp8x8_to_16bit<Elt>(kr[s].x, kr[s].y);
+                ka[2 * s + 1] = fp8x8_to_16bit<Elt>(kr[s].z, kr[s].w);
+            } else {
+                ka[s] = kr[s];
+            }
+        }
         float sc[RC][4];
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(kr[s], qb[c][s], sacc);
+            for (int s = 0; s < KS; ++s) sacc = MfmaQK<Elt>::run(ka[s], qb[c][s], sacc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[c][r] = sacc[r] * p.scale_log2;
         }
@@ -326,12 +373,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int dh = 0; dh < DH; ++dh) {
-                const uint4 w = vr[r][dh];
                 float vf[8];
-                vf[0] = Elt::lo(w.x); vf[1] = Elt::hi(w.x);
-                vf[2] = Elt::lo(w.y); vf[3] = Elt::hi(w.y);
-                vf[4] = Elt::lo(w.z); vf[5] = Elt::hi(w.z);
-                vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
+                if constexpr (F8) {
+                    const uint2 w = vr[r][dh];
+                    const f32x2_t a = fp8x2_lo(w.x), bb = fp8x2_hi(w.x);
+                    const f32x2_t c2 = fp8x2_lo(w.y), d2 = fp8x2_hi(w.y);
+                    vf[0] = a[0]; vf[1] = a[1]; vf[2] = bb[0]; vf[3] = bb[1];
+                    vf[4] = c2[0]; vf[5] = c2[1]; vf[6] = d2[0]; vf[7] = d2[1];
+                } else {
+                    const uint4 w = vr[r][dh];
+                    vf[0] = Elt::lo(w.x); vf[1] = Elt::hi(w.x);
+                    vf[2] = Elt::lo(w.y); vf[3] = Elt::hi(w.y);
+                    vf[4] = Elt::lo(w.z); vf[5] = Elt::hi(w.z);
+                    vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
+                }
                 if constexpr (NG == 0) {
 #pragma unroll
                     for (int c = 0; c < RC; ++c)
@@ -351,23 +406,47 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
     };
 
-    // Two register buffers, loop rotated so that its head waits for buffer a
-    // while buffer b is in flight.  The loop has a single exit and its loads
+    // Register buffers in rotation.  The loop has a single exit and its loads
     // are unconditional (past the end they load nothing, see load_tile): an
     // exit or a guarded load in the middle of the body makes the compiler
     // drain every outstanding load (vmcnt(0)) at the loop head, which leaves
-    // one tile in flight instead of two.
+    // one tile in flight instead of more.
     int j = wave;
-    uint4 ka[KS], va[4][DH], kb[KS], vb[4][DH];
-    if (j < ntiles) {
-        load_tile(j, first[0], ka, va);
-        load_tile(j + kWaves, first[1], kb, vb);
-    }
-    for (; j < ntiles; j += 2 * kWaves) {
-        process(j, ka, va);
-        load_tile(j + 2 * kWaves, block_of(j + 2 * kWaves), ka, va);
-        if (j + kWaves < ntiles) process(j + kWaves, kb, vb);
-        load_tile(j + 3 * kWaves, block_of(j + 3 * kWaves), kb, vb);
+    if constexpr (S == 2) {
+        // two buffers, loop rotated so that its head waits for buffer a
+        // while buffer b is in flight
+        uint4 ka[KL], kb[KL];
+        VRaw va[4][DH], vb[4][DH];
+        if (j < ntiles) {
+            load_tile(j, first[0], ka, va);
+            load_tile(j + kWaves, first[1], kb, vb);
+        }
+        for (; j < ntiles; j += 2 * kWaves) {
+            process(j, ka, va);
+            load_tile(j + 2 * kWaves, block_of(j + 2 * kWaves), ka, va);
+            if (j + kWaves < ntiles) process(j + kWaves, kb, vb);
+            load_tile(j + 3 * kWaves, block_of(j + 3 * kWaves), kb, vb);
+        }
+    } else {
+        // S buffers: each step refills the buffer freed by the previous step,
+        // then processes the oldest, so S-1 tiles are in flight meanwhile
+        uint4 kbuf[S][KL];
+        VRaw vbuf[S][4][DH];
+        if (j < ntiles) {
+            load_tile(j, first[0], kbuf[0], vbuf[0]);
+            load_tile(j + kWaves, first[1], kbuf[1], vbuf[1]);
+#pragma unroll
+            for (int st = 2; st < S - 1; ++st)
+                load_tile(j + st * kWaves, block_of(j + st * kWaves), kbuf[st], vbuf[st]);
+        }
+        for (; j < ntiles; j += S * kWaves) {
+#pragma unroll
+            for (int st = 0; st < S; ++st) {
+                const int jn = j + (st + S - 1) * kWaves;
+                load_tile(jn, block_of(jn), kbuf[(st + S - 1) % S], vbuf[(st + S - 1) % S]);
+                if (j + st * kWaves < ntiles) process(j + st * kWaves, kbuf[st], vbuf[st]);
+            }
+        }
     }
 
     // full denominator of each lane row (all four lane groups hold the same m)
@@ -448,16 +527,18 @@ using EltT = FP16;
 #endif
 constexpr int kHead = PDA_HEAD;
 
+constexpr bool kF8 = PDA_KV_FP8 != 0;
+
 template <bool ALIGNED, bool BUF, int NG, int RC>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
     const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC>), grid,
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC, kF8>), grid,
                               dim3(kThreads), lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC>), grid,
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC, kF8>), grid,
                            dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
@@ -480,9 +561,14 @@ static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream
 
 #define PDA_CAT2(a, b, c) a##_##b##_##c
 #define PDA_CAT(a, b, c) PDA_CAT2(a, b, c)
-hipError_t PDA_CAT(launch_decode_mfma, PDA_DTYPE, PDA_HEAD)(bool aligned, const DecodeParams& p,
-                                                            int batch, hipStream_t stream,
-                                                            hipEvent_t e0, hipEvent_t e1) {
+#if PDA_KV_FP8
+#define PDA_MFMA_LAUNCHER launch_decode_mfma8
+#else
+#define PDA_MFMA_LAUNCHER launch_decode_mfma
+#endif
+hipError_t PDA_CAT(PDA_MFMA_LAUNCHER, PDA_DTYPE, PDA_HEAD)(bool aligned, const DecodeParams& p,
+                                                           int batch, hipStream_t stream,
+                                                           hipEvent_t e0, hipEvent_t e1) {
     // Buffer loads (past-the-end prefetches cost nothing) measured faster at
     // head sizes up to 128, and at 256 when a wave holds at most two tiles;
     // for long partitions at 256 the compiler schedules the global-load form

@@ -25,6 +25,10 @@ struct BF16 {
     __device__ static inline uint16_t from_float(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
     }
+    // two fp32 values that are bf16 values (low 16 bits zero) packed exactly
+    __device__ static inline uint32_t pack_exact(float lo, float hi) {
+        return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    }
 };
 
 struct FP16 {
@@ -41,7 +45,26 @@ struct FP16 {
     __device__ static inline uint16_t from_float(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));  // round to nearest even
     }
+    // two fp32 values that are fp16 values packed exactly (no rounding occurs)
+    __device__ static inline uint32_t pack_exact(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
 };
+
+// ---- fp8 E4M3 (OCP) KV bytes -------------------------------------------
+// The hardware conversion decodes the OCP E4M3 format exactly (every E4M3
+// value, subnormals and NaN included, is an fp32 value, and also a bf16 and
+// an fp16 value), two bytes of a 32-bit word at a time.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline f32x2_t fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
+__device__ inline f32x2_t fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
+// 8 E4M3 bytes -> 8 elements of the 16-bit type, exactly
+template <typename Elt>
+__device__ inline uint4 fp8x8_to_16bit(uint32_t w0, uint32_t w1) {
+    const f32x2_t a = fp8x2_lo(w0), b = fp8x2_hi(w0), c = fp8x2_lo(w1), d = fp8x2_hi(w1);
+    return make_uint4(Elt::pack_exact(a[0], a[1]), Elt::pack_exact(b[0], b[1]),
+                      Elt::pack_exact(c[0], c[1]), Elt::pack_exact(d[0], d[1]));
+}
 
 // 2^x with the hardware instruction (v_exp_f32).  Arguments here are
 // differences of scores from a running max, so they are <= 0; -inf gives 0,
@@ -82,6 +105,28 @@ __device__ inline uint4 load_row16_buf(const char* base, uint32_t off, bool vali
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
 #endif
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 8 bytes of a row (an fp8 V chunk), plain and through a buffer resource
+// (same contract as load_row16 / load_row16_buf).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint2 load_row8(const char* ptr) {
+#if PDA_VALU_NT
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ptr));
+#else
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(ptr);
+#endif
+    return make_uint2(v.x, v.y);
+}
+__device__ inline uint2 load_row8_buf(const char* base, uint32_t off, bool valid) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base), (short)0, valid ? 0x7fffffff : 0, kBufferWord3);
+#if PDA_VALU_NT
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 2);  // nt
+#else
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, off, 0, 0);
+#endif
+    return make_uint2(v.x, v.y);
 }
 
 // Device-scope (all XCDs) store and load of fp32 workspace data: the store
@@ -356,8 +401,9 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
         }
         // a row with no token in this partition (a causal row ending before
         // it) has den == 0: its normalised partial is 0, and its weight l = 0
-        // keeps it out of the merge
-        const float on = den > 0.f ? o / den : 0.f;
+        // keeps it out of the merge.  v_scale (1 for 16-bit KV) dequantises
+        // fp8 V; the merge is linear in o, so it applies to partials too.
+        const float on = den > 0.f ? o / den * p.v_scale : 0.f;
         const int64_t row = row_index(p, b, g, h0 + i);
         if (direct) {
             out16[row * D + d] = Elt::from_float(on);

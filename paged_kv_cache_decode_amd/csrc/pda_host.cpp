@@ -2,6 +2,7 @@
 // workspace layout and the kernel launches behind the C ABI of pda.h.
 #include <algorithm>
 #include <atomic>
+#include <math.h>
 #include <stdint.h>
 
 #include "pda_common.h"
@@ -33,6 +34,35 @@ hipError_t launch_decode_mfma_1_128(bool, const DecodeParams&, int, hipStream_t,
                                        hipEvent_t);
 hipError_t launch_decode_mfma_1_256(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
                                        hipEvent_t);
+
+hipError_t launch_decode_mfma8_0_64(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                    hipEvent_t);
+hipError_t launch_decode_mfma8_0_128(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                     hipEvent_t);
+hipError_t launch_decode_mfma8_0_256(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                     hipEvent_t);
+hipError_t launch_decode_mfma8_1_64(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                    hipEvent_t);
+hipError_t launch_decode_mfma8_1_128(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                     hipEvent_t);
+hipError_t launch_decode_mfma8_1_256(bool, const DecodeParams&, int, hipStream_t, hipEvent_t,
+                                     hipEvent_t);
+
+// fp8 KV: the translation units built with PDA_KV_FP8
+static hipError_t launch_decode_mfma_fp8(int dtype, int head_size, bool aligned,
+                                         const DecodeParams& p, int batch, hipStream_t s,
+                                         hipEvent_t e0, hipEvent_t e1) {
+    if (dtype == PDA_BF16) {
+        if (head_size == 64) return launch_decode_mfma8_0_64(aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_mfma8_0_128(aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_mfma8_0_256(aligned, p, batch, s, e0, e1);
+    } else {
+        if (head_size == 64) return launch_decode_mfma8_1_64(aligned, p, batch, s, e0, e1);
+        if (head_size == 128) return launch_decode_mfma8_1_128(aligned, p, batch, s, e0, e1);
+        if (head_size == 256) return launch_decode_mfma8_1_256(aligned, p, batch, s, e0, e1);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_mfma(int dtype, int head_size, bool aligned, const DecodeParams& p,
                               int batch, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
@@ -74,6 +104,8 @@ constexpr int32_t kMaxGridYZ = 65535;
 constexpr int kValuMaxGroup = 8;
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool kv_fp8(const pda_shape_t* s) { return s->kv_dtype == PDA_KV_FP8_E4M3; }
 int64_t round256(int64_t x) { return cdiv64(x, 256) * 256; }
 
 // block sizes that are multiples of 16 tokens take the one-lookup-per-round
@@ -112,7 +144,7 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
     if (pl->merge != PDA_MERGE_FUSED && pl->merge != PDA_MERGE_KERNEL) return PDA_ERR_INVALID;
     const int R = (int)rows_of(s);
     if (pl->variant == PDA_VARIANT_VALU) {
-        if (R > kValuMaxGroup) return PDA_ERR_UNSUPPORTED;
+        if (R > kValuMaxGroup || kv_fp8(s)) return PDA_ERR_UNSUPPORTED;
         const int64_t lds = (int64_t)decode_lds_bytes(s->head_size, valu_group_pad(R),
                                                       (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
@@ -144,7 +176,9 @@ int device_cu_count(int32_t* cu) {
 
 DecodeParams make_params(const pda_shape_t* s, const pda_plan_t* pl, float scale) {
     DecodeParams p{};
-    p.scale_log2 = scale * 1.4426950408889634f;
+    // fp8 KV: q.(k_scale * K) = k_scale * (q.K), folded into the score scale
+    p.scale_log2 = (kv_fp8(s) ? scale * s->k_scale : scale) * 1.4426950408889634f;
+    p.v_scale = kv_fp8(s) ? s->v_scale : 1.0f;
     p.num_q_heads = s->num_q_heads;
     p.num_kv_heads = s->num_kv_heads;
     p.group = s->num_q_heads / s->num_kv_heads;
@@ -181,6 +215,10 @@ int pda_check_shape(const pda_shape_t* s) {
     if (s->head_size != 64 && s->head_size != 128 && s->head_size != 256)
         return PDA_ERR_UNSUPPORTED;
     if (s->dtype != PDA_BF16 && s->dtype != PDA_FP16) return PDA_ERR_UNSUPPORTED;
+    if (s->kv_dtype != PDA_KV_SAME && s->kv_dtype != PDA_KV_FP8_E4M3) return PDA_ERR_UNSUPPORTED;
+    if (kv_fp8(s) && !(s->k_scale > 0.f && s->k_scale < INFINITY && s->v_scale > 0.f &&
+                       s->v_scale < INFINITY))
+        return PDA_ERR_INVALID;
     if (s->num_q_heads / s->num_kv_heads > PDA_MAX_GROUP) return PDA_ERR_UNSUPPORTED;
     if (s->q_len > PDA_MAX_ROWS || rows_of(s) > PDA_MAX_ROWS) return PDA_ERR_UNSUPPORTED;
     if ((int64_t)s->max_seq_len > (int64_t)s->max_blocks_per_seq * s->block_size)
@@ -199,9 +237,9 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     // the rule documented in pda.h
     const int64_t R = rows_of(s);
     const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
-    const bool mfma = R > PDA_VALU_MAX_GROUP ||
+    const bool mfma = kv_fp8(s) || R > PDA_VALU_MAX_GROUP ||
                       (R >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
-    const int64_t bpt = 4 * (int64_t)s->head_size;
+    const int64_t bpt = (kv_fp8(s) ? 2 : 4) * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
     const int64_t t_min = std::max(align, (PDA_WG_MIN_BYTES / bpt / align) * align);
     const int64_t t_many = std::max(t_min, (PDA_WG_MANY_BYTES / bpt / align) * align);
@@ -288,11 +326,15 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool aligned = block_aligned(s);
-    hipError_t e = pl->variant == PDA_VARIANT_MFMA
-                       ? launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
-                                            ev0, ev1)
-                       : launch_decode_valu(s->dtype, s->head_size, valu_group_pad(p.rows),
-                                            aligned, p, s->num_seqs, st, ev0, ev1);
+    hipError_t e;
+    if (pl->variant == PDA_VARIANT_MFMA)
+        e = kv_fp8(s) ? launch_decode_mfma_fp8(s->dtype, s->head_size, aligned, p, s->num_seqs,
+                                               st, ev0, ev1)
+                      : launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
+                                           ev0, ev1);
+    else
+        e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(p.rows), aligned, p,
+                               s->num_seqs, st, ev0, ev1);
     if (e != hipSuccess) return PDA_ERR_LAUNCH;
     if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
         e = launch_merge(s->dtype, s->head_size, p, (int)(s->num_seqs * q_len_of(s)), st);
@@ -380,7 +422,7 @@ const char* pda_status_string(int status) {
 #define PDA_BUILD_FLAGS "unknown"
 #endif
 const char* pda_build_id(void) {
-    return "libpda 0.3.0; target gfx950; variants valu|mfma; merge fused|kernel; flags " PDA_BUILD_FLAGS;
+    return "libpda 0.4.0; target gfx950; variants valu|mfma; kv bf16|fp16|fp8e4m3; merge fused|kernel; flags " PDA_BUILD_FLAGS;
 }
 
 }  // extern "C"

@@ -27,16 +27,19 @@ def run(case: kvgen.Case, plan=None, out=None) -> torch.Tensor:
     out = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
                                 case.seq_lens_t, case.scale, out=out,
                                 max_seq_len=case.max_seq_len, plan=plan,
-                                sliding_window=case.sliding_window)
+                                sliding_window=case.sliding_window, k_scale=case.k_scale,
+                                v_scale=case.v_scale)
     torch.cuda.synchronize()
     return out
 
 
 def reference(case: kvgen.Case, seqs=None) -> np.ndarray:
     q, k, v, lens = kvgen.oracle_inputs(case, seqs)
+    sc = (case.k_scale, case.v_scale) if case.kv_dtype == "fp8" else None
     if case.q_len > 1:
-        return oracle.decode_multi(q, k, v, lens, case.scale, window=case.sliding_window)
-    return oracle.decode(q, k, v, lens, case.scale, window=case.sliding_window)
+        return oracle.decode_multi(q, k, v, lens, case.scale, window=case.sliding_window,
+                                   kv_scales=sc)
+    return oracle.decode(q, k, v, lens, case.scale, window=case.sliding_window, kv_scales=sc)
 
 
 def check(case: kvgen.Case, got: torch.Tensor, ref: np.ndarray = None, seqs=None,

@@ -53,10 +53,12 @@ def test_plan_matches_oracle_plan(D):
         n = int(rng.choice([1, 1, 2, 3, 8]))
         if n * G > 32:
             n = 1
+        f8 = bool(rng.integers(0, 4) == 0)
         shape = pda.make_shape(B, Hkv * G, Hkv, D, bs, 10, mbs, L, "bf16", sliding_window=W,
-                               q_len=n)
+                               q_len=n, kv_dtype="fp8" if f8 else "same", k_scale=0.5,
+                               v_scale=0.25)
         got = pda.pda_plan_for_cus(shape, cu)
-        P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n)
+        P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n, kv_fp8=f8)
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
         assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv, q_len=n)
         assert got.merge == pda.PDA_MERGE_KERNEL
@@ -91,12 +93,17 @@ BAD_SHAPES = [
     (dict(q_len=-1), pda.PDA_ERR_INVALID),
     (dict(q_len=9), pda.PDA_ERR_UNSUPPORTED),                       # 9 x 4 rows > 32
     (dict(q_len=33, num_q_heads=8), pda.PDA_ERR_UNSUPPORTED),      # 33 rows
+    (dict(kv_dtype=2), pda.PDA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=1, k_scale=0.0, v_scale=1.0), pda.PDA_ERR_INVALID),
+    (dict(kv_dtype=1, k_scale=1.0, v_scale=float("inf")), pda.PDA_ERR_INVALID),
+    (dict(kv_dtype=1, k_scale=float("nan"), v_scale=1.0), pda.PDA_ERR_INVALID),
 ]
 
 
 def _shape(**kw):
     base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_size=128, block_size=16,
-                num_blocks=16, max_blocks_per_seq=4, max_seq_len=64, dtype=0, q_len=1)
+                num_blocks=16, max_blocks_per_seq=4, max_seq_len=64, dtype=0, q_len=1,
+                kv_dtype=0, k_scale=1.0, v_scale=1.0)
     base.update(kw)
     return pda.PdaShape(**base)
 
@@ -173,3 +180,23 @@ def test_fastdiv_method_is_exact():
         hi = (ns * np.uint64(mul)) >> np.uint64(32)
         q = (hi + ns) >> np.uint64(l)
         assert np.array_equal(q, ns // np.uint64(d)), d
+
+
+def test_fp8_kv_plans_matrix_core_and_rejects_valu():
+    shape = pda.make_shape(64, 32, 8, 128, 16, 100, 2048, 32768, "bf16", kv_dtype="fp8",
+                           k_scale=0.01, v_scale=0.02)
+    plan = pda.pda_plan_for_cus(shape, 256)
+    assert plan.variant == pda.PDA_VARIANT_MFMA
+    # K and V bytes per token halve: the 256 KiB partitions hold 1024 tokens
+    assert plan.tokens_per_partition == 1024
+    plan.variant = pda.PDA_VARIANT_VALU
+    lib = pda.load_library()
+    rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(plan), 1, 1, 1, 1, 1,
+                                         1.0, 1, 1, 1 << 30, None)
+    assert rc == pda.PDA_ERR_UNSUPPORTED
+
+
+def test_q_len_zero_is_one_row():
+    a = pda.pda_plan_for_cus(pda.make_shape(3, 32, 8, 128, 16, 10, 64, 1000, q_len=0), 256)
+    b = pda.pda_plan_for_cus(pda.make_shape(3, 32, 8, 128, 16, 10, 64, 1000, q_len=1), 256)
+    assert a.as_dict() == b.as_dict()

@@ -327,3 +327,62 @@ def test_multi_row_last_row_is_the_plain_decode_and_one_row_is_decode():
     q1 = q[:, :1]
     assert np.array_equal(oracle.decode_multi(q1, k, v, L, case.scale)[:, 0],
                           oracle.decode(q[:, 0], k, v, L, case.scale))
+
+
+# ---- fp8 KV: the OCP E4M3 decode and dequantisation ------------------------
+
+def test_e4m3_closed_form_values():
+    v = oracle.e4m3_value
+    assert v(0x00) == 0.0 and v(0x80) == 0.0 and np.signbit(v(0x80))
+    assert v(0x38) == 1.0 and v(0xB8) == -1.0 and v(0xC0) == -2.0
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0          # largest finite
+    assert v(0x01) == 2.0 ** -9                              # smallest subnormal
+    assert v(0x07) == 7 / 8 * 2.0 ** -6                      # largest subnormal
+    assert v(0x08) == 2.0 ** -6                              # smallest normal
+    assert v(0x39) == 1.125 and v(0x30) == 0.5
+    assert np.isnan(v(0x7F)) and np.isnan(v(0xFF))           # the only NaNs
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_value(codes)
+    assert np.isnan(vals).sum() == 2
+    finite = vals[~np.isnan(vals)]
+    assert np.all(np.isfinite(finite)) and finite.max() == 448.0
+
+
+def test_e4m3_matches_torch_float8_e4m3fn_on_every_code():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = oracle.e4m3_value(codes.numpy())
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+def test_fp8_decode_closed_form_equal_keys():
+    """All K bytes equal: every score is equal, so each output row is the
+    plain mean of its sequence's dequantised V rows."""
+    B, Hq, Hkv, D = 2, 4, 2, 64
+    lens = [37, 5]
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    k = [np.full((Hkv, L, D), 0x38, dtype=np.uint8) for L in lens]      # all 1.0
+    v = [rng.integers(0, 256, size=(Hkv, L, D)).astype(np.uint8) for L in lens]
+    for x in v:
+        x[(x & 0x7F) == 0x7F] = 0x38                                       # no NaN codes
+    ks, vs = 0.25, 0.0625
+    got = oracle.decode(q, k, v, lens, 0.1, kv_scales=(ks, vs))
+    for b, L in enumerate(lens):
+        vals = oracle.e4m3_value(v[b]) * vs                                # [Hkv, L, D]
+        for h in range(Hq):
+            ref = vals[h // (Hq // Hkv)].mean(axis=0)
+            assert np.max(np.abs(got[b, h] - ref)) <= 1e-6 * np.max(np.abs(ref))
+
+
+def test_fp8_generator_round_trip():
+    """The generator's fp8 codes decode to within one E4M3 rounding step of
+    the drawn values (relative half-ULP 2^-4 for normals)."""
+    case = kvgen.make_case(2, 8, 2, 64, 16, [40, 33], seed=5, kv_dtype="fp8")
+    assert case.k_cache.dtype == torch.float8_e4m3fn
+    q, k, v, lens = kvgen.oracle_inputs(case)
+    assert k[0].dtype == np.uint8
+    kk = oracle.dequantize_e4m3(k[0], case.k_scale)
+    assert np.isfinite(kk).all() and np.max(np.abs(kk)) <= 448 * case.k_scale * (1 + 1e-6)
