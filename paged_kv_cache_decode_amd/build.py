@@ -18,9 +18,14 @@ LIB = os.path.join(HERE, "libpda.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
-# -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_fma_f32 and kin)
+# -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_fma_f32 and kin).
+# -amdgpu-mfma-vgpr-form: matrix-core accumulators in VGPRs.  With them in
+# AGPRs the compiler copied every accumulator out and back on each tile around
+# the softmax rescale (v_accvgpr_read/write, 64-128 VALU moves per tile); the
+# VGPR form has none and measured faster on every matrix-core shape.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
@@ -37,7 +42,8 @@ def _units(csrc=CSRC):
                           [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}", "-DPDA_KV_FP8=1"]))
     units.append((os.path.join(csrc, "pda_merge.hip"), "merge.o", []))
     units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
-    flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops"])
+    flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops",
+                                   "-amdgpu-mfma-vgpr-form"])
     units.append((os.path.join(csrc, "pda_host.cpp"), "host.o",
                    ["-x", "hip", f'-DPDA_BUILD_FLAGS="{flags}"']))
     return units
