@@ -108,12 +108,12 @@ extern "C" {
 
 /* ---- kernel variants --------------------------------------------------- */
 /* PDA_VARIANT_VALU: QK^T with packed dot2 and wavefront DPP reductions, PV
- *   with per-lane fp32 FMAs; G <= PDA_VALU_MAX_GROUP.
- * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 (bf16/fp16 inputs, the
- *   packed rows padded to 16 per tile) and PV with fp32 weights and exact
- *   fp32 V, on v_mfma_f32_4x4x1_16b_f32 blocks of 4 rows for R <= 4 (and
- *   R <= 8 at head sizes up to 128), else on v_mfma_f32_16x16x4_f32 with the
- *   rows padded to 16 per tile; R <= PDA_MAX_ROWS.
+ *   with per-lane fp32 FMAs and fp32 weights; G <= PDA_VALU_MAX_GROUP.
+ * PDA_VARIANT_MFMA: QK^T on v_mfma_f32_16x16x32 and PV on
+ *   v_mfma_f32_16x16x16 (bf16/fp16 inputs, the packed rows padded to 16 per
+ *   chunk, fp32 accumulation); the softmax weights enter PV rounded to the
+ *   16-bit type (round to nearest even), and the denominator sums those
+ *   rounded weights; R <= PDA_MAX_ROWS.
  * R = q_len * G is the number of rows a unit packs (G for plain decode);
  * the VALU variant serves R <= PDA_VALU_MAX_GROUP. */
 #define PDA_VARIANT_VALU 1

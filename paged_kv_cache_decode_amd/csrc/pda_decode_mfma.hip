@@ -16,14 +16,18 @@
 //   softmax  online, exp2 domain; the running max per head is shared by the
 //         four lanes that hold that head; the accumulator is rescaled only
 //         when some max grew.
-//   PV    O = P V on v_mfma_f32_16x16x4_f32: the exp'd scores are already in
-//         the A-operand layout (row = l%16, k = token 4(l/16) + r), and
-//         round r of V loads token 4(l/16) + r, 16 bytes per lane, so each of
-//         the lane's 8 elements is the B operand of one MFMA.  V never needs
-//         a transpose; P stays fp32 (no rounding of the weights to 16 bits).
+//   PV    O^T = V^T P^T on v_mfma_f32_16x16x16_{bf16,f16}, one MFMA per
+//         element e of the lanes' 8-element V chunks: round r of V loads
+//         token 4(l/16) + r, elements d = 8*(l%16) + e, so element e of the
+//         lane's four rounds is exactly its A operand (d-row l%16, tokens
+//         4(l/16) .. +4), and the exp'd scores the lane holds (row l%16,
+//         the same four tokens) are exactly its B operand.  Neither V nor P
+//         moves between lanes; the weights are rounded to the 16-bit type
+//         (V is exact), and the denominator sums the rounded weights, so the
+//         output stays a convex combination of V rows.
 //
-// VALU work per tile is reduced to the 16-bit -> fp32 conversion of V and the
-// softmax bookkeeping, independent of the row count.
+// VALU work per tile is reduced to the repacking of V halves and the softmax
+// bookkeeping, independent of the row count.
 //
 // fp8 KV (F8): K and V rows are OCP E4M3 bytes.  A lane's 16-byte K load
 // then holds 16 elements, d = 64*s2 + 16*q4 .. +16, decoded exactly to the
@@ -81,41 +85,40 @@ struct MfmaQK<FP16> {
     }
 };
 
+template <typename Elt>
+struct MfmaPV;
+template <>
+struct MfmaPV<BF16> {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    __device__ static inline f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                         __builtin_bit_cast(i16x4_t, b), c, 0, 0,
+                                                         0);
+    }
+};
+template <>
+struct MfmaPV<FP16> {
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    __device__ static inline f32x4_t run(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    }
+};
+
+// 32-bit word i of a 16-byte chunk (i a compile-time constant after unrolling)
+__device__ inline uint32_t word_of(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 // The element type and head size are template parameters of the kernel so
 // that every instantiation has its own symbol across translation units.
-// 16-lane-row operand exchange for the 4-head-block PV: lane l takes the
-// value of lane (l & 0b110011) | (grp << 2), i.e. the lane of its own token
-// group (bits 4-5) that holds head 4*grp + (l & 3) (bits 2-3 select the head
-// group).  ds_swizzle in bit-mask mode: and 0x13, or grp << 2, within 32 lanes.
-template <int GRP>
-__device__ inline float take_head_of_group(float x) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x13 | (GRP << 7)));
-}
-
-// Sum of a lane value over the four token groups (lanes l, l^16, l^32,
-// l^48), in the fixed order (g0 + g1) + (g2 + g3), with the gfx950 row and
-// half swaps (VALU, no LDS).
-__device__ inline float sum_token_groups(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false,
-                                                    false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // The unit's R = q_len * G rows (row r: query position r / G, head r % G)
 // are packed in RC chunks of 16 (RC = 2 for R > 16): each K tile feeds RC
-// QK products, and each chunk keeps its own softmax state and accumulators.
-// NG = 0: PV on v_mfma_f32_16x16x4_f32 with each chunk padded to 16 rows.
-// NG = 1, 2 (R <= 8, RC = 1): PV on v_mfma_f32_4x4x1_16b_f32, NG blocks of 4
-// rows: block (lanes 4k..4k+3) = one token (the lane's V row of the round) x
-// 4 columns of d, rows = the 4 rows of a block; no padding to 16, a quarter
-// of the matrix-core cycles per block.  Each lane group (l / 16) accumulates
-// over its own tokens; the four partial sums are added once at the end.
-template <typename Elt, int D, bool ALIGNED, bool BUF, int NG, int RC, bool F8>
+// QK and RC PV products, and each chunk keeps its own softmax state and
+// accumulators.
+template <typename Elt, int D, bool ALIGNED, bool BUF, int RC, bool F8>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-    static_assert(RC == 1 || (RC == 2 && NG == 0), "two row chunks use the padded PV form");
+    static_assert(RC == 1 || RC == 2, "one or two 16-row chunks");
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
     constexpr int EB = F8 ? 1 : 2;             // KV bytes per element
@@ -256,13 +259,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         return ALIGNED ? tile_block(p, trow, tile_start(jj)) : TileBlock{0, 0};
     };
 
-    // NG = 0: oacc[c][dh][e][r] = O[row 16c + 4*q4 + r][d = dh*128 + 8*c16 + e]
-    // NG > 0: oacc[grp][dh][e][i] = O[row 4*grp + i][same d], partial over
-    //         the tokens of lane group q4
-    constexpr int NA = NG == 0 ? RC : NG;
-    f32x4_t oacc[NA][DH][8];
+    // oacc[c][dh][e][i] = O[row 16c + c16][d = dh*128 + 8*(4*q4 + i) + e]
+    // (for D = 64 the d-rows 4*q4 + i >= CW repeat the first CW)
+    f32x4_t oacc[RC][DH][8];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int a = 0; a < RC; ++a)
 #pragma unroll
         for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
@@ -319,89 +320,58 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
             for (int c = 0; c < RC; ++c) {
+                // every accumulator register of the lane belongs to its own row
                 const float alpha = fast_exp2(m[c] - mn[c]);
                 l[c] *= alpha;
-                if constexpr (NG == 0) {
-                    // the accumulator rows of this lane are rows 16c + 4*q4 + r
-                    float ar[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+                for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                    for (int dh = 0; dh < DH; ++dh)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) oacc[c][dh][e][r] *= ar[r];
-                } else {
-                    // rows 4*grp + i: their factors sit in lanes 4*grp + i
-#pragma unroll
-                    for (int grp = 0; grp < NG; ++grp) {
-                        float ar[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            ar[i] = __int_as_float(
-                                __builtin_amdgcn_readlane(__float_as_int(alpha), 4 * grp + i));
-#pragma unroll
-                        for (int dh = 0; dh < DH; ++dh)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) oacc[grp][dh][e][i] *= ar[i];
-                    }
-                }
+                    for (int e = 0; e < 8; ++e) oacc[c][dh][e] *= alpha;
                 m[c] = mn[c];
             }
         }
-        float pr[RC][4];
+        // B operand: the lane's four weights of row 16c + c16 (tokens
+        // 4*q4 + r), rounded to the 16-bit type; the denominator sums the
+        // rounded values, in token order
+        uint2 pb[RC];
 #pragma unroll
-        for (int c = 0; c < RC; ++c)
+        for (int c = 0; c < RC; ++c) {
+            uint32_t h[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[c][r] = fast_exp2(sc[c][r] - m[c]);
-                l[c] += pr[c][r];
-            }
-        // A operand of the 4-row blocks: lane 4k + i needs row 4*grp + i
-        float pa[NG > 0 ? NG : 1][4];
-        if constexpr (NG > 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pa[0][r] = take_head_of_group<0>(pr[0][r]);
-                if constexpr (NG > 1) pa[1][r] = take_head_of_group<1>(pr[0][r]);
-            }
+            for (int r = 0; r < 4; ++r) h[r] = Elt::from_float(fast_exp2(sc[c][r] - m[c]));
+            pb[c].x = h[0] | (h[1] << 16);
+            pb[c].y = h[2] | (h[3] << 16);
+            l[c] += Elt::lo(pb[c].x);
+            l[c] += Elt::hi(pb[c].x);
+            l[c] += Elt::lo(pb[c].y);
+            l[c] += Elt::hi(pb[c].y);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int dh = 0; dh < DH; ++dh) {
+            // the lane's four V rounds (tokens 4*q4 + r) as 16-bit elements
+            uint4 w[4];
 #pragma unroll
-            for (int dh = 0; dh < DH; ++dh) {
-                float vf[8];
-                if constexpr (F8) {
-                    const uint2 w = vr[r][dh];
-                    const f32x2_t a = fp8x2_lo(w.x), bb = fp8x2_hi(w.x);
-                    const f32x2_t c2 = fp8x2_lo(w.y), d2 = fp8x2_hi(w.y);
-                    vf[0] = a[0]; vf[1] = a[1]; vf[2] = bb[0]; vf[3] = bb[1];
-                    vf[4] = c2[0]; vf[5] = c2[1]; vf[6] = d2[0]; vf[7] = d2[1];
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (F8)
+                    w[r] = fp8x8_to_16bit<Elt>(vr[r][dh].x, vr[r][dh].y);
+                else
+                    w[r] = vr[r][dh];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // A operand: element e of the four rounds, tokens in order
+                const int wi = e / 2;
+                uint2 a;
+                if (e % 2 == 0) {
+                    a.x = (word_of(w[0], wi) & 0xffffu) | (word_of(w[1], wi) << 16);
+                    a.y = (word_of(w[2], wi) & 0xffffu) | (word_of(w[3], wi) << 16);
                 } else {
-                    const uint4 w = vr[r][dh];
-                    vf[0] = Elt::lo(w.x); vf[1] = Elt::hi(w.x);
-                    vf[2] = Elt::lo(w.y); vf[3] = Elt::hi(w.y);
-                    vf[4] = Elt::lo(w.z); vf[5] = Elt::hi(w.z);
-                    vf[6] = Elt::lo(w.w); vf[7] = Elt::hi(w.w);
+                    a.x = (word_of(w[0], wi) >> 16) | (word_of(w[1], wi) & 0xffff0000u);
+                    a.y = (word_of(w[2], wi) >> 16) | (word_of(w[3], wi) & 0xffff0000u);
                 }
-                if constexpr (NG == 0) {
 #pragma unroll
-                    for (int c = 0; c < RC; ++c)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            oacc[c][dh][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                pr[c][r], vf[e], oacc[c][dh][e], 0, 0, 0);
-                } else {
-#pragma unroll
-                    for (int grp = 0; grp < NG; ++grp)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            oacc[grp][dh][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(
-                                pa[grp][r], vf[e], oacc[grp][dh][e], 0, 0, 0);
-                }
+                for (int c = 0; c < RC; ++c)
+                    oacc[c][dh][e] = MfmaPV<Elt>::run(a, pb[c], oacc[c][dh][e]);
             }
         }
     };
@@ -455,52 +425,23 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         l[c] += __shfl_xor(l[c], 16);
         l[c] += __shfl_xor(l[c], 32);
     }
-    if constexpr (NG > 0) {  // add the four lane groups' partial sums
-#pragma unroll
-        for (int grp = 0; grp < NG; ++grp)
-#pragma unroll
-            for (int dh = 0; dh < DH; ++dh)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        oacc[grp][dh][e][i] = sum_token_groups(oacc[grp][dh][e][i]);
-    }
 
     // merge the wavefronts and write the unit's result, rows in chunks
     for (int h0 = 0; h0 < R; h0 += kHeadChunk) {
         const int hn = min(kHeadChunk, R - h0);
-        if constexpr (NG == 0) {
-            if (c16 < CW) {
 #pragma unroll
-                for (int c = 0; c < RC; ++c)
+        for (int c = 0; c < RC; ++c) {
+            const int hi = 16 * c + c16 - h0;
+            if (hi < 0 || hi >= hn) continue;
+            float* row = red + (wave * kHeadChunk + hi) * (D + 2);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int hi = 16 * c + 4 * q4 + r - h0;
-                        if (hi < 0 || hi >= hn) continue;
-                        float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+            for (int i = 0; i < 4; ++i) {
+                if (4 * q4 + i >= CW) continue;  // repeated d-rows (D = 64)
 #pragma unroll
-                        for (int dh = 0; dh < DH; ++dh)
+                for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                row[dh * 128 + 8 * c16 + e] = oacc[c][dh][e][r];
-                    }
-            }
-        } else {
-            if (q4 == 0 && c16 < CW) {
-#pragma unroll
-                for (int grp = 0; grp < NG; ++grp)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int hi = 4 * grp + i - h0;
-                        if (hi < 0 || hi >= hn) continue;
-                        float* row = red + (wave * kHeadChunk + hi) * (D + 2);
-#pragma unroll
-                        for (int dh = 0; dh < DH; ++dh)
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                row[dh * 128 + 8 * c16 + e] = oacc[grp][dh][e][i];
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        row[dh * 128 + 8 * (4 * q4 + i) + e] = oacc[c][dh][e][i];
             }
         }
         if (q4 == 0) {
@@ -529,34 +470,26 @@ constexpr int kHead = PDA_HEAD;
 
 constexpr bool kF8 = PDA_KV_FP8 != 0;
 
-template <bool ALIGNED, bool BUF, int NG, int RC>
+template <bool ALIGNED, bool BUF, int RC>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
     const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC, kF8>), grid,
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8>), grid,
                               dim3(kThreads), lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, NG, RC, kF8>), grid,
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8>), grid,
                            dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 
-// PV form by rows per unit: 4-row blocks for up to 4 rows, and for up to 8
-// at head sizes up to 128, where they take at most half the matrix-core
-// cycles of the padded 16-row form; the padded form otherwise (two 4-row
-// blocks at head size 256 need more registers than a wave has: their
-// accumulators hold four token-group partials per output), in two chunks
-// beyond 16 rows.
+// One 16-row chunk for up to 16 rows per unit, two beyond.
 template <bool ALIGNED, bool BUF>
 static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-    if (p.rows <= 4) return launch_one<ALIGNED, BUF, 1, 1>(p, batch, stream, start, stop);
-    if constexpr (kHead <= 128)
-        if (p.rows <= 8) return launch_one<ALIGNED, BUF, 2, 1>(p, batch, stream, start, stop);
-    if (p.rows <= 16) return launch_one<ALIGNED, BUF, 0, 1>(p, batch, stream, start, stop);
-    return launch_one<ALIGNED, BUF, 0, 2>(p, batch, stream, start, stop);
+    if (p.rows <= 16) return launch_one<ALIGNED, BUF, 1>(p, batch, stream, start, stop);
+    return launch_one<ALIGNED, BUF, 2>(p, batch, stream, start, stop);
 }
 
 #define PDA_CAT2(a, b, c) a##_##b##_##c

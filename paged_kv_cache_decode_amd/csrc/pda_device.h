@@ -363,7 +363,7 @@ __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, i
 // ---- MFMA tile geometry --------------------------------------------------
 // A 16-token tile.  K rows feed the A operand of v_mfma_f32_16x16x32 (S^T =
 // K Q^T): lane l reads token l%16, elements 32s + 8(l/16) .. +8 for k-step s.
-// V rows feed the B operand of v_mfma_f32_16x16x4_f32 (O^T... O = P V): for
+// V rows feed the A operand of v_mfma_f32_16x16x16 (O^T = V^T P^T): for
 // round r lane l reads token 4(l/16) + r, elements dh*128 + 8*(l%16 % CW) .. +8,
 // CW = min(16, D/8) column groups per 128-wide half dh.
 template <int D>
