@@ -143,9 +143,10 @@ extern "C" {
  *   P      = max(1, ceil(Lmax / T_p))
  *   i.e. when one round of C workgroups, one per compute unit, covers the
  *   job at <= 1 MiB each, use exactly that round (the split-KV partition
- *   count comes from the CU count); otherwise cut the job into 256 KiB
+ *   count comes from the CU count); otherwise cut the job into 1 MiB
  *   workgroups and let the hardware dispatcher balance them over many
- *   rounds.  (Every extra round, and every second workgroup on a CU, exposes
+ *   rounds (1 MiB measured faster than 256 and 512 KiB for the batched
+ *   shapes).  (Every extra round, and every second workgroup on a CU, exposes
  *   a workgroup's start-up and epilogue again and doubles the partials the
  *   merge reads; one workgroup per CU measured fastest for both variants.)
  * Partition p of (b, g) covers tokens [base + p*T_p, min(base + (p+1)*T_p,
@@ -173,7 +174,7 @@ extern "C" {
 #define PDA_MFMA_MIN_GROUP  2
 #define PDA_MFMA_MAX_UNITS  128
 #define PDA_WG_MIN_BYTES    (64 * 1024)
-#define PDA_WG_MANY_BYTES   (256 * 1024)
+#define PDA_WG_MANY_BYTES   (1024 * 1024)
 #define PDA_WG_ONE_BYTES    (1024 * 1024)
 
 #define PDA_MERGE_FUSED   0

@@ -17,7 +17,7 @@ VALU_MAX_GROUP = 8
 MFMA_MIN_GROUP = 2
 MFMA_MAX_UNITS = 128
 WG_MIN_BYTES = 64 * 1024
-WG_MANY_BYTES = 256 * 1024
+WG_MANY_BYTES = 1024 * 1024
 WG_ONE_BYTES = 1024 * 1024
 VALU, MFMA = 1, 2
 

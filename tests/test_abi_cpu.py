@@ -187,8 +187,8 @@ def test_fp8_kv_plans_matrix_core_and_rejects_valu():
                            k_scale=0.01, v_scale=0.02)
     plan = pda.pda_plan_for_cus(shape, 256)
     assert plan.variant == pda.PDA_VARIANT_MFMA
-    # K and V bytes per token halve: the 256 KiB partitions hold 1024 tokens
-    assert plan.tokens_per_partition == 1024
+    # K and V bytes per token halve: the 1 MiB partitions hold 4096 tokens
+    assert plan.tokens_per_partition == 4096
     plan.variant = pda.PDA_VARIANT_VALU
     lib = pda.load_library()
     rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(plan), 1, 1, 1, 1, 1,
