@@ -127,11 +127,13 @@ extern "C" {
  * sliding window W > 0 (the union of the rows' windows, rounded out to the
  * 16-token grid the partitions start on):
  *
- * Variant: MFMA for fp8 KV, if R > PDA_VALU_MAX_GROUP, or if R >=
+ * Variant: MFMA for fp8 KV, if R > PDA_VALU_PLAN_ROWS, or if R >=
  *   PDA_MFMA_MIN_GROUP and B*Hkv <= PDA_MFMA_MAX_UNITS (the lighter VALU
  *   load of the matrix cores pays); VALU otherwise (one row per unit, where
- *   the VALU kernel has the least to do, or many units over many rounds,
- *   where its higher occupancy pays).
+ *   the VALU kernel has the least to do, or 2 to 4 rows over many units and
+ *   rounds, where its higher occupancy pays).  Beyond 4 rows the VALU
+ *   kernel's per-row arithmetic outweighs its occupancy (measured 1.6x
+ *   slower at 8 rows over 512 units).
  * Partition size, with ALIGN = PDA_TP_ALIGN and bpt = 4*D, or 2*D for fp8 KV
  *   (K and V bytes per token of one KV head):
  *   T_min  = max(ALIGN, floor(PDA_WG_MIN_BYTES  / bpt / ALIGN) * ALIGN)
@@ -139,7 +141,8 @@ extern "C" {
  *   T_one  = max(T_many, floor(PDA_WG_ONE_BYTES / bpt / ALIGN) * ALIGN)
  *   P_fill = ceil(C / (B * Hkv))
  *   T_fill = max(T_min, roundup(ceil(Lmax / P_fill), ALIGN))
- *   T_p    = T_fill if T_fill <= T_one else T_many
+ *   T_p    = T_fill if T_fill <= T_one else T_many, raised if needed to
+ *            roundup(ceil(Lmax / 65535), ALIGN) (at most 65535 partitions)
  *   P      = max(1, ceil(Lmax / T_p))
  *   i.e. when one round of C workgroups, one per compute unit, covers the
  *   job at <= 1 MiB each, use exactly that round (the split-KV partition
@@ -152,8 +155,10 @@ extern "C" {
  * Partition p of (b, g) covers tokens [base + p*T_p, min(base + (p+1)*T_p,
  * seq_lens[b])), base = 0 without a window, else lo_0 (the first row's
  * window start) rounded down to a multiple of 16; it is empty when that
- * range is.  The grid of the main kernel is
- * (P, Hkv, B).  When P == 1 the main kernel writes `out` directly and no
+ * range is.  The grid of the main kernel is (Hkv, B, P), the partition
+ * index slowest, so that the empty partitions of short sequences are
+ * dispatched after every live one; a plan has at most 65535 partitions
+ * (PDA_ERR_UNSUPPORTED otherwise).  When P == 1 the main kernel writes `out` directly and no
  * workspace is used; otherwise it writes fp32 partials that are merged with
  * the log-sum-exp rule, either
  *   PDA_MERGE_KERNEL by a separate merge kernel on the same stream (the
@@ -172,6 +177,7 @@ extern "C" {
 #define PDA_TILE            16
 #define PDA_TP_ALIGN        64
 #define PDA_MFMA_MIN_GROUP  2
+#define PDA_VALU_PLAN_ROWS  4
 #define PDA_MFMA_MAX_UNITS  128
 #define PDA_WG_MIN_BYTES    (64 * 1024)
 #define PDA_WG_MANY_BYTES   (1024 * 1024)

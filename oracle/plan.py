@@ -15,10 +15,12 @@ so the rule is this library's own; what the pages fix is the reason for it:
 TP_ALIGN = 64
 VALU_MAX_GROUP = 8
 MFMA_MIN_GROUP = 2
+VALU_PLAN_ROWS = 4
 MFMA_MAX_UNITS = 128
 WG_MIN_BYTES = 64 * 1024
 WG_MANY_BYTES = 1024 * 1024
 WG_ONE_BYTES = 1024 * 1024
+MAX_PARTITIONS = 65535
 VALU, MFMA = 1, 2
 
 
@@ -28,11 +30,11 @@ def _cdiv(a: int, b: int) -> int:
 
 def variant(num_seqs: int, num_kv_heads: int, group: int, q_len: int = 1,
             kv_fp8: bool = False) -> int:
-    """MFMA for fp8 KV, above the VALU row limit, or for R = q_len * G >= 2
+    """MFMA for fp8 KV, above 4 rows per unit, or for R = q_len * G >= 2
     rows with at most 128 units."""
     units = num_seqs * num_kv_heads
     rows = max(1, q_len) * group
-    if kv_fp8 or rows > VALU_MAX_GROUP or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
+    if kv_fp8 or rows > VALU_PLAN_ROWS or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
         return MFMA
     return VALU
 
@@ -67,6 +69,7 @@ def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_
     else:
         t_fill = max(t_min, _cdiv(_cdiv(lspan, p_fill), TP_ALIGN) * TP_ALIGN)
         t_p = t_fill if t_fill <= t_one else t_many
+        t_p = max(t_p, _cdiv(_cdiv(lspan, MAX_PARTITIONS), TP_ALIGN) * TP_ALIGN)
     p = max(1, _cdiv(lspan, t_p))
     return p, t_p, var
 

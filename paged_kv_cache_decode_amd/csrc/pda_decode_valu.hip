@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     float* red = smem;                                                  // [kWaves][GP][D+2]
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
 
-    const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // grid (Hkv, B, P): the partition index varies slowest (see the launcher)
+    const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int c = lane % LPT, r = lane / LPT;
@@ -297,7 +298,11 @@ constexpr int kHead = PDA_HEAD;
 template <int GP, bool ALIGNED>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
-    const dim3 grid(p.num_partitions, p.num_kv_heads, batch);
+    // Workgroups are dispatched in grid order, partition by partition: the
+    // empty partitions of shorter sequences come after the live partitions of
+    // every sequence instead of between them, where each one measured to cost
+    // tens of ns of the whole launch (mixed lengths at batch 64: 16% faster).
+    const dim3 grid(p.num_kv_heads, batch, p.num_partitions);
     const uint32_t lds = (uint32_t)decode_lds_bytes(kHead, GP, p.tbl_capacity);
     if (start || stop)
         hipExtLaunchKernelGGL((decode_valu_kernel<EltT, kHead, GP, ALIGNED>), grid, dim3(kThreads),

@@ -139,7 +139,8 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
         return PDA_ERR_INVALID;
     if ((int64_t)pl->num_partitions * pl->tokens_per_partition < plan_span(s))
         return PDA_ERR_INVALID;
-    if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen)
+    if ((int64_t)pl->num_partitions * pl->tokens_per_partition > (int64_t)2 * kMaxSeqLen ||
+        pl->num_partitions > kMaxGridYZ)
         return PDA_ERR_UNSUPPORTED;
     if (pl->merge != PDA_MERGE_FUSED && pl->merge != PDA_MERGE_KERNEL) return PDA_ERR_INVALID;
     const int R = (int)rows_of(s);
@@ -237,7 +238,7 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     // the rule documented in pda.h
     const int64_t R = rows_of(s);
     const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
-    const bool mfma = kv_fp8(s) || R > PDA_VALU_MAX_GROUP ||
+    const bool mfma = kv_fp8(s) || R > PDA_VALU_PLAN_ROWS ||
                       (R >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
     const int64_t bpt = (kv_fp8(s) ? 2 : 4) * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
@@ -250,6 +251,8 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     if (span > 0) {
         const int64_t t_fill = std::max(t_min, cdiv64(cdiv64(span, p_fill), align) * align);
         tp = t_fill <= t_one ? t_fill : t_many;
+        // at most kMaxGridYZ partitions (a grid dimension)
+        tp = std::max(tp, cdiv64(cdiv64(span, kMaxGridYZ), align) * align);
     }
     int64_t P = cdiv64(span, tp);
     if (P < 1) P = 1;

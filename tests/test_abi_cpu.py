@@ -200,3 +200,20 @@ def test_q_len_zero_is_one_row():
     a = pda.pda_plan_for_cus(pda.make_shape(3, 32, 8, 128, 16, 10, 64, 1000, q_len=0), 256)
     b = pda.pda_plan_for_cus(pda.make_shape(3, 32, 8, 128, 16, 10, 64, 1000, q_len=1), 256)
     assert a.as_dict() == b.as_dict()
+
+
+def test_plan_caps_partitions_at_the_grid_limit():
+    """The partition index is a grid dimension: at most 65535 partitions,
+    the partition size raised to keep within it."""
+    L = 1 << 30
+    shape = pda.make_shape(1, 8, 1, 256, 16, 1 << 26, L // 16, L)
+    got = pda.pda_plan_for_cus(shape, 256)
+    P, T, var = oplan.partition(1, 1, 8, 256, L, 256)
+    assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
+    assert P <= 65535 and P * T >= L and T % 64 == 0
+    bad = pda.PdaPlan(num_partitions=65536, tokens_per_partition=16384, variant=pda.PDA_VARIANT_MFMA,
+                      merge=pda.PDA_MERGE_KERNEL, cu_count=0, workspace_bytes=0)
+    lib = pda.load_library()
+    rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(bad), 1, 1, 1, 1, 1,
+                                         1.0, 1, 1, 1 << 40, None)
+    assert rc == pda.PDA_ERR_UNSUPPORTED
