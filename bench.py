@@ -218,6 +218,39 @@ def measured_traffic(variant: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 2048)):
+    """Achievable HBM read bandwidth: the library's streaming-read probe over
+    one buffer of `nbytes` (16x the 256 MB MALL), timed with HIP events over
+    `calls` back-to-back reads after two untimed ones, for each grid size in
+    `grids`; the best rate is the achievable figure."""
+    import torch
+    import paged_kv_cache_decode_amd as pda
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rates = {}
+    for wg in grids:
+        for _ in range(2):
+            pda.pda_read_probe(src, sink, wg)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(calls):
+            pda.pda_read_probe(src, sink, wg)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / calls
+        rates[wg] = nbytes / (ms * 1e-3) / 1e9
+    del src
+    torch.cuda.empty_cache()
+    best = max(rates, key=rates.get)
+    return {"GBps": round(rates[best], 1), "frac_of_peak": round(rates[best] / PEAK_GBS, 4),
+            "bytes": nbytes, "workgroups": best,
+            "GBps_by_workgroups": {str(k): round(v, 1) for k, v in rates.items()},
+            "what": "one streaming read of a 4 GiB buffer with the decode kernels' 16-byte "
+                    "non-temporal loads (pda_read_probe), best grid size"}
+
+
 def cpu_baseline(case, seconds):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -250,6 +283,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS),
                     help="the timed workload (default: the headline one)")
     args = ap.parse_args()
@@ -322,6 +356,11 @@ def main():
 
     kbytes = r["kv_bytes"]
     achieved = kbytes / (r["kernel_ms"] * 1e-3) / 1e9
+    probe = None
+    if not args.no_probe:
+        log("timing the streaming-read probe")
+        probe = read_probe()
+        probe["decode_kernel_frac_of_probe"] = round(achieved / probe["GBps"], 4)
     line = {
         "metric": "achieved KV HBM GB/s (% of MI355X peak) and us/call at 32K-context decode",
         "value": head["GBps"],
@@ -350,6 +389,7 @@ def main():
                      "kernel_us": round(r["kernel_ms"] * 1e3, 3),
                      "algorithmic_bytes_per_launch": kbytes},
         "cpu_baseline": cpu,
+        "read_probe": probe,
         "parity_rel_linf_vs_oracle": parity,
         "extra": extra,
     }

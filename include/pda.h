@@ -290,6 +290,18 @@ int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan, in
                             int32_t* trace_slot, int32_t* trace_part,
                             int32_t* trace_range, void* stream);
 
+/* HBM streaming-read probe (a measurement aid, not part of the decode):
+ * reads the `bytes` (a positive multiple of 16) at device pointer `src`
+ * once, with the decode kernels' non-temporal 16-byte loads, in a
+ * grid-stride loop over `workgroups` workgroups of 256 threads, and XORs the
+ * 32-bit words of the buffer into the device word `sink` (which the caller
+ * zeroes first: the result is then the XOR of all words, independent of the
+ * schedule).  Timing it over a buffer far larger than the 256 MB MALL gives
+ * the achievable read bandwidth the decode's roofline fraction can be set
+ * against.  Asynchronous on `stream`; PDA_ERR_INVALID for a null pointer, a
+ * bad size or 0 / more than 2^20 workgroups. */
+int pda_read_probe(const void* src, int64_t bytes, void* sink, int32_t workgroups, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* pda_status_string(int status);
 

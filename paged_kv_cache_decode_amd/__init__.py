@@ -103,6 +103,8 @@ def load_library():
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_build_id.argtypes = []
     lib.pda_build_id.restype = ctypes.c_char_p
+    lib.pda_read_probe.argtypes = [P, ctypes.c_int64, P, ctypes.c_int32, P]
+    lib.pda_read_probe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -279,6 +281,17 @@ def paged_decode_attn_workspace_init(workspace, stream=None):
     rc = load_library().paged_decode_attn_workspace_init(_ptr(workspace), nbytes, _stream(stream))
     if rc != PDA_OK:
         raise PdaError(rc, "paged_decode_attn_workspace_init")
+
+
+def pda_read_probe(src, sink, workgroups: int = 2048, stream=None):
+    """HBM streaming-read probe: read the device tensor `src` once and XOR
+    its 32-bit words into the int32 device tensor `sink` (one element,
+    zeroed by the caller).  Asynchronous on the stream."""
+    nbytes = src.numel() * src.element_size()
+    rc = load_library().pda_read_probe(_ptr(src), nbytes, _ptr(sink), int(workgroups),
+                                       _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "pda_read_probe")
 
 
 def paged_decode_attn_timed(shape: PdaShape, plan: Optional[PdaPlan], q, k_cache, v_cache,

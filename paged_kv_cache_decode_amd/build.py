@@ -42,6 +42,7 @@ def _units(csrc=CSRC):
                           [f"-DPDA_DTYPE={dt}", f"-DPDA_HEAD={hd}", "-DPDA_KV_FP8=1"]))
     units.append((os.path.join(csrc, "pda_merge.hip"), "merge.o", []))
     units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
+    units.append((os.path.join(csrc, "pda_probe.hip"), "probe.o", []))
     flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops",
                                    "-amdgpu-mfma-vgpr-form"])
     units.append((os.path.join(csrc, "pda_host.cpp"), "host.o",
