@@ -77,6 +77,7 @@ struct DecodeParams {
     int32_t num_blocks;        // NB: block ids are clamped into [0, NB)
     int32_t rows;              // R = q_len * G rows per unit
     float v_scale;             // fp8 V scale (1 for 16-bit KV); k_scale is in scale_log2
+    int32_t lds_floor;         // dynamic LDS of the decode launch is at least this (bytes)
     int64_t block_stride;      // Hkv * bs * D elements
     int32_t head_stride;       // bs * D elements
 };

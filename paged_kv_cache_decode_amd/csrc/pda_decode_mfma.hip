@@ -479,7 +479,8 @@ static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t strea
     // every sequence instead of between them, where each one measured to cost
     // tens of ns of the whole launch (mixed lengths at batch 64: 16% faster).
     const dim3 grid(p.num_kv_heads, batch, p.num_partitions);
-    const uint32_t lds = (uint32_t)mfma_lds_bytes(kHead, p.tbl_capacity);
+    const size_t own = mfma_lds_bytes(kHead, p.tbl_capacity);
+    const uint32_t lds = (uint32_t)(own > (size_t)p.lds_floor ? own : (size_t)p.lds_floor);
     if (start || stop)
         hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8>), grid,
                               dim3(kThreads), lds, stream, start, stop, 0, p);
