@@ -201,8 +201,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // Tile jj >= ntiles is a prefetch past the end: with buffer loads (BUF)
     // it loads nothing (zeros, no memory access); otherwise it re-reads the
     // last tile.  Either way process() never sees it.  Buffer loads need a
-    // wave-uniform block base (the aligned path); the launcher picks them
-    // where they measured faster (see launch_one).
+    // wave-uniform block base: the launcher uses them on the aligned path.
     static_assert(ALIGNED || !BUF, "buffer loads need the aligned path");
     constexpr bool kBuf = BUF;
     auto tile_start = [&](int jj) { return t0 + (kBuf ? jj : min(jj, ntiles - 1)) * TT; };
@@ -508,14 +507,11 @@ static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream
 hipError_t PDA_CAT(PDA_MFMA_LAUNCHER, PDA_DTYPE, PDA_HEAD)(bool aligned, const DecodeParams& p,
                                                            int batch, hipStream_t stream,
                                                            hipEvent_t e0, hipEvent_t e1) {
-    // Buffer loads (past-the-end prefetches cost nothing) measured faster at
-    // head sizes up to 128, and at 256 when a wave holds at most two tiles;
-    // for long partitions at 256 the compiler schedules the global-load form
-    // better (its next-tile loads issue earlier), ~7% faster.
-    const bool buf = kHead <= 128 || p.tokens_per_part <= 2 * kWaves * 16;
+    // The aligned path uses buffer loads (past-the-end prefetches load
+    // nothing); they measured faster at every head size (at 256 since the
+    // 16x16x16 PV: 29.7 -> 28.7 us at the low-parallelism layer).
     if (!aligned) return launch_pv<false, false>(p, batch, stream, e0, e1);
-    return buf ? launch_pv<true, true>(p, batch, stream, e0, e1)
-               : launch_pv<true, false>(p, batch, stream, e0, e1);
+    return launch_pv<true, true>(p, batch, stream, e0, e1);
 }
 
 }  // namespace pda
