@@ -379,47 +379,77 @@ __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + 
 // ---- unit epilogue shared by the decode kernels ------------------------
 // Combine the kWaves per-wave states of rows h0 .. h0+hn-1 of unit (b, g),
 // staged in LDS as red[w][i][0..D) = unnormalised O, red[w][i][D] = running
-// max m (exp2 domain), red[w][i][D+1] = denominator l, in a fixed order, and
-// write either the 16-bit output (one partition) or the fp32 partial.
+// max m (exp2 domain), red[w][i][D+1] = denominator l (red_heads rows per
+// wave, hn <= min(red_heads, 8)), in a fixed order, and write either the
+// 16-bit output (one partition) or the fp32 partial.  32 threads per row
+// (8 rows at a time): each computes its row's wave weights once and then
+// D/32 consecutive elements, read from LDS in pairs and stored together.
 template <typename Elt, int D>
 __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, int red_heads,
                                        int h0, int hn, int b, int g, int part) {
-    uint16_t* out16 = static_cast<uint16_t*>(p.out);
-    const bool direct = p.num_partitions == 1;
-    for (int idx = threadIdx.x; idx < hn * D; idx += blockDim.x) {
-        const int i = idx / D, d = idx - i * D;
-        float M = -FLT_MAX;
+    constexpr int kTpr = 32;                 // threads per row
+    constexpr int kDpt = D / kTpr;           // consecutive elements per thread: 2, 4 or 8
+    static_assert(kDpt % 2 == 0 && kThreads == 8 * kTpr, "rows of 32 threads, element pairs");
+    const int i = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * kDpt;
+    if (i >= hn) return;
+    float mw[kWaves];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * red_heads + i) * (D + 2) + D]);
-        float o = 0.f, den = 0.f;
+    for (int w = 0; w < kWaves; ++w) mw[w] = red[(w * red_heads + i) * (D + 2) + D];
+    float M = -FLT_MAX;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float* row = red + (w * red_heads + i) * (D + 2);
-            const float wt = fast_exp2(row[D] - M);
-            den += row[D + 1] * wt;
-            o += row[d] * wt;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+    float wt[kWaves], den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        wt[w] = fast_exp2(mw[w] - M);
+        den += red[(w * red_heads + i) * (D + 2) + D + 1] * wt[w];
+    }
+    // a row with no token in this partition (a causal row ending before it)
+    // has den == 0: its normalised partial is 0, and its weight l = 0 keeps
+    // it out of the merge.  v_scale (1 for 16-bit KV) dequantises fp8 V; the
+    // merge is linear in o, so it applies to partials too.
+    const float f = den > 0.f ? p.v_scale / den : 0.f;
+    float o[kDpt];
+#pragma unroll
+    for (int e = 0; e < kDpt; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float2* src = reinterpret_cast<const float2*>(red + (w * red_heads + i) * (D + 2) + d0);
+#pragma unroll
+        for (int e = 0; e < kDpt / 2; ++e) {
+            const float2 v = src[e];
+            o[2 * e] += v.x * wt[w];
+            o[2 * e + 1] += v.y * wt[w];
         }
-        // a row with no token in this partition (a causal row ending before
-        // it) has den == 0: its normalised partial is 0, and its weight l = 0
-        // keeps it out of the merge.  v_scale (1 for 16-bit KV) dequantises
-        // fp8 V; the merge is linear in o, so it applies to partials too.
-        const float on = den > 0.f ? o / den * p.v_scale : 0.f;
-        const int64_t row = row_index(p, b, g, h0 + i);
-        if (direct) {
-            out16[row * D + d] = Elt::from_float(on);
-        } else {
-            const int64_t prow = row * p.num_partitions + part;
-            if (p.fused_merge) {  // read back by another workgroup of this launch
-                store_coherent(p.ws_o + prow * D + d, on);
-                if (d == 0) {
-                    store_coherent(p.ws_ml + prow * 2, M);
-                    store_coherent(p.ws_ml + prow * 2 + 1, den);
-                }
-            } else {              // read by the merge kernel after this launch
-                p.ws_o[prow * D + d] = on;
-                if (d == 0) { p.ws_ml[prow * 2] = M; p.ws_ml[prow * 2 + 1] = den; }
-            }
+    }
+#pragma unroll
+    for (int e = 0; e < kDpt; ++e) o[e] *= f;
+    const int64_t row = row_index(p, b, g, h0 + i);
+    if (p.num_partitions == 1) {
+        uint32_t pk[kDpt / 2];
+#pragma unroll
+        for (int e = 0; e < kDpt / 2; ++e)
+            pk[e] = (uint32_t)Elt::from_float(o[2 * e]) |
+                    ((uint32_t)Elt::from_float(o[2 * e + 1]) << 16);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + row * D + d0);
+#pragma unroll
+        for (int e = 0; e < kDpt / 2; ++e) dst[e] = pk[e];
+        return;
+    }
+    const int64_t prow = row * p.num_partitions + part;
+    float* dst = p.ws_o + prow * D + d0;
+    if (p.fused_merge) {  // read back by another workgroup of this launch
+#pragma unroll
+        for (int e = 0; e < kDpt; ++e) store_coherent(dst + e, o[e]);
+        if (d0 == 0) {
+            store_coherent(p.ws_ml + prow * 2, M);
+            store_coherent(p.ws_ml + prow * 2 + 1, den);
         }
+    } else {              // read by the merge kernel after this launch
+#pragma unroll
+        for (int e = 0; e < kDpt / 2; ++e)
+            reinterpret_cast<float2*>(dst)[e] = make_float2(o[2 * e], o[2 * e + 1]);
+        if (d0 == 0) reinterpret_cast<float2*>(p.ws_ml)[prow] = make_float2(M, den);
     }
 }
 
