@@ -322,6 +322,8 @@ def main():
         small_steps = max(20, args.steps // 4)
         specs = [(f"cfg2 Hq{hq} 32K", lambda hq=hq: configs.cfg2(hq, L, device="cuda"))
                  for hq in (8, 16, 24)]
+        specs += [(f"cfg2 Hq32 {n}", lambda n=n: configs.cfg2(32, n, device="cuda"))
+                  for n in configs.CFG2_LENS]
         specs += [("cfg3 B1 bf16 32K", lambda: configs.cfg3(1, L, device="cuda")),
                   ("cfg3 B1 fp16 32K", lambda: configs.cfg3(1, L, dtype="fp16", device="cuda")),
                   ("cfg3 B8 bf16 32K", lambda: configs.cfg3(8, L, device="cuda"))]
@@ -347,12 +349,16 @@ def main():
             extra[name] = summary(name, c, rr)
             del c, rr
             torch.cuda.empty_cache()
-        ladder = [(extra[f"cfg4 {n}"]["context_tokens"], extra[f"cfg4 {n}"]["us_per_call"])
-                  for n in configs.CFG4_LENS]
-        xs = np.array([a for a, _ in ladder], dtype=np.float64)
-        ys = np.array([b for _, b in ladder], dtype=np.float64)
-        slope = float(np.polyfit(xs, ys, 1)[0])
-        extra["cfg4 slope us per context token"] = round(slope, 6)
+        # decode time added per token of context: the slope of us/call over each ladder
+        def slope(points):
+            xs = np.array([a for a, _ in points], dtype=np.float64)
+            ys = np.array([b for _, b in points], dtype=np.float64)
+            return round(float(np.polyfit(xs, ys, 1)[0]), 6)
+        extra["cfg4 slope us per context token"] = slope(
+            [(extra[f"cfg4 {n}"]["context_tokens"], extra[f"cfg4 {n}"]["us_per_call"])
+             for n in configs.CFG4_LENS])
+        extra["headline slope us per context token"] = slope(
+            [(n, extra[f"cfg2 Hq32 {n}"]["us_per_call"]) for n in configs.CFG2_LENS])
 
     kbytes = r["kv_bytes"]
     achieved = kbytes / (r["kernel_ms"] * 1e-3) / 1e9

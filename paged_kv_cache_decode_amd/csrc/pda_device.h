@@ -454,31 +454,127 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
 }
 
 // Log-sum-exp merge of the Pb partials (o_p normalised, m_p, l_p in the exp2
-// domain) of the R rows of unit (b, g), one output element per thread and
-// step, partitions in index order with a running max:
+// domain) of the R rows of unit (b, g):
 //   out = sum_p l_p 2^(m_p - M) o_p / sum_p l_p 2^(m_p - M),  M = max_p m_p
-// (0 for a row with no token at all).
+// (0 for a row with no token at all), partitions summed in index order.
+// Every load of a step is issued before any is used: first all (m, l) pairs
+// of the unit, from which one thread per row forms the weights in LDS; then
+// each thread loads all Pb partials of four consecutive elements of a row
+// (16-byte device-scope loads) and sums them.  Up to kMergePairs (row,
+// partition) pairs; beyond that, one element per thread and step with a
+// running max.
+constexpr int kMergePairs = 1024;
+constexpr int kMergeUnroll = 16;  // partitions whose loads are in flight together
+
+// 16 bytes of the workspace at base + off (16-byte aligned), read at device
+// scope (sc1: not from a possibly stale L2 line) through a buffer resource.
+// `base` must be wave-uniform (it is made so: a lane-varying resource would
+// make the compiler loop over the lanes' distinct values).
+__device__ inline float4 load_coherent16(const float* base, uint32_t off) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    // each half through uint32_t: the builtin returns int, and a low half
+    // with bit 31 set would otherwise sign-extend into the high half
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t ua = (hi << 32) | lo;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(ua), (short)0, 0x7fffffff, kBufferWord3);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 16);  // sc1
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
 template <typename Elt, int D>
 __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
+    __shared__ float s_w[kMergePairs];
+    __shared__ float s_f[PDA_MAX_ROWS];
     uint16_t* out16 = static_cast<uint16_t*>(p.out);
-    for (int idx = threadIdx.x; idx < p.rows * D; idx += blockDim.x) {
-        const int i = idx / D, d = idx - i * D;
-        const int64_t row = row_index(p, b, g, i);
-        const float* ml = p.ws_ml + row * p.num_partitions * 2;
-        const float* po = p.ws_o + row * p.num_partitions * D + d;
-        float M = -FLT_MAX, o = 0.f, den = 0.f;
-#pragma unroll 8
-        for (int q = 0; q < Pb; ++q) {
-            const float mq = load_coherent(ml + 2 * q), lq = load_coherent(ml + 2 * q + 1);
-            const float oq = load_coherent(po + (int64_t)q * D);
-            const float mn = fmaxf(M, mq);
-            const float sc = fast_exp2(M - mn);
-            const float w = lq * fast_exp2(mq - mn);
-            o = o * sc + w * oq;
-            den = den * sc + w;
-            M = mn;
+    const int R = p.rows, P = p.num_partitions;
+    // byte span of the unit's partials from its first row: the 16-byte loads
+    // take 32-bit offsets from that row
+    const int64_t span = (row_index(p, b, g, R - 1) - row_index(p, b, g, 0) + 1) * P * D * 4;
+    if (R * Pb > kMergePairs || span >= ((int64_t)1 << 31)) {
+        for (int idx = threadIdx.x; idx < R * D; idx += blockDim.x) {
+            const int i = idx / D, d = idx - i * D;
+            const int64_t row = row_index(p, b, g, i);
+            const float* ml = p.ws_ml + row * P * 2;
+            const float* po = p.ws_o + row * P * D + d;
+            float M = -FLT_MAX, o = 0.f, den = 0.f;
+            for (int q = 0; q < Pb; ++q) {
+                const float mq = load_coherent(ml + 2 * q), lq = load_coherent(ml + 2 * q + 1);
+                const float oq = load_coherent(po + (int64_t)q * D);
+                const float mn = fmaxf(M, mq);
+                const float sc = fast_exp2(M - mn);
+                const float w = lq * fast_exp2(mq - mn);
+                o = o * sc + w * oq;
+                den = den * sc + w;
+                M = mn;
+            }
+            out16[row * D + d] = Elt::from_float(den > 0.f ? o / den : 0.f);
         }
-        out16[row * D + d] = Elt::from_float(den > 0.f ? o / den : 0.f);
+        return;
+    }
+    // (m, l) of every (row, partition) pair: s_w holds m, then the weight
+    constexpr int KP = (kMergePairs + kThreads - 1) / kThreads;
+    float lv[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+        const int idx = threadIdx.x + k * kThreads;
+        if (idx < R * Pb) {
+            const int i = idx / Pb, q = idx - i * Pb;
+            const float* ml = p.ws_ml + (row_index(p, b, g, i) * P + q) * 2;
+            s_w[idx] = load_coherent(ml);
+            lv[k] = load_coherent(ml + 1);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {  // the row's max, held in s_f for the next step
+        float M = -FLT_MAX;
+        for (int q = 0; q < Pb; ++q) M = fmaxf(M, s_w[threadIdx.x * Pb + q]);
+        s_f[threadIdx.x] = M;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {  // each pair's m is read and replaced by its own thread
+        const int idx = threadIdx.x + k * kThreads;
+        if (idx < R * Pb) s_w[idx] = lv[k] * fast_exp2(s_w[idx] - s_f[idx / Pb]);
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {  // the row's normalisation, sums in partition order
+        float den = 0.f;
+        for (int q = 0; q < Pb; ++q) den += s_w[threadIdx.x * Pb + q];
+        s_f[threadIdx.x] = den > 0.f ? 1.f / den : 0.f;
+    }
+    __syncthreads();
+    constexpr int D4 = D / 4;
+    // partials of the unit's first row: the wave-uniform base of the loads
+    const int64_t row0 = row_index(p, b, g, 0);
+    const float* base = p.ws_o + row0 * P * D;
+    for (int it = threadIdx.x; it < R * D4; it += blockDim.x) {
+        const int i = it / D4, c = it - i * D4;
+        const int64_t row = row_index(p, b, g, i);
+        const uint32_t off0 = (uint32_t)(((row - row0) * P * D + 4 * c) * sizeof(float));
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int q0 = 0; q0 < Pb; q0 += kMergeUnroll) {
+            float4 v[kMergeUnroll];
+#pragma unroll
+            for (int u = 0; u < kMergeUnroll; ++u) {
+                const int q = min(q0 + u, Pb - 1);  // past Pb: re-read the last, weight 0
+                v[u] = load_coherent16(base, off0 + (uint32_t)(q * D * sizeof(float)));
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeUnroll; ++u) {
+                const float w = q0 + u < Pb ? s_w[i * Pb + q0 + u] : 0.f;
+                acc.x += w * v[u].x; acc.y += w * v[u].y;
+                acc.z += w * v[u].z; acc.w += w * v[u].w;
+            }
+        }
+        const float f = s_f[i];
+        uint16_t* dst = out16 + row * D + 4 * c;
+        dst[0] = Elt::from_float(acc.x * f);
+        dst[1] = Elt::from_float(acc.y * f);
+        dst[2] = Elt::from_float(acc.z * f);
+        dst[3] = Elt::from_float(acc.w * f);
     }
 }
 
