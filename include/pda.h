@@ -231,7 +231,8 @@ int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
 
 /* Zero `bytes` of a device workspace on `stream` (asynchronously): the state
  * a workspace must be in before its first fused call.  Call it once after
- * allocating a workspace, outside any HIP graph capture. */
+ * allocating a workspace.  It is a kernel launch (not a memset), so it may
+ * also be captured into a HIP graph. */
 int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream);
 
 /* The decode step, under the device's own plan.

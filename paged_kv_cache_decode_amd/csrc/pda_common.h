@@ -109,6 +109,8 @@ hipError_t launch_decode_mfma(int dtype, int head_size, bool aligned, const Deco
                               int batch, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_merge(int dtype, int head_size, const DecodeParams& p, int batch,
                         hipStream_t stream);
+// zero `bytes` at device pointer `dst` with a fill kernel on `stream`
+hipError_t launch_zero_fill(void* dst, int64_t bytes, hipStream_t stream);
 // rows: 0 = the VALU kernel's rows, 1 = the MFMA kernel's K rows, 2 = its V rows
 hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
                         hipStream_t stream);

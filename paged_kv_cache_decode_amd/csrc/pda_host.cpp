@@ -281,7 +281,8 @@ int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
 int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream) {
     if (bytes < 0 || (bytes > 0 && !workspace)) return PDA_ERR_INVALID;
     if (bytes == 0) return PDA_OK;
-    hipError_t e = hipMemsetAsync(workspace, 0, (size_t)bytes, static_cast<hipStream_t>(stream));
+    // a fill kernel, not a memset: a caller may capture this into a HIP graph
+    hipError_t e = launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
 }
 
