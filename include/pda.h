@@ -86,7 +86,8 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define PDA_OK                0
 #define PDA_ERR_INVALID      -1  /* null pointer, non-positive size, Hq % Hkv != 0, bad plan */
-#define PDA_ERR_UNSUPPORTED  -2  /* head size not 64/128/256, G > PDA_MAX_GROUP, bad dtype */
+#define PDA_ERR_UNSUPPORTED  -2  /* head size not 64/128/256, G > PDA_MAX_GROUP, bad dtype,
+                                    block_size * head_size > INT32_MAX */
 #define PDA_ERR_WORKSPACE    -3  /* workspace_bytes smaller than the plan needs */
 #define PDA_ERR_LAUNCH       -4  /* a kernel launch failed (hipGetLastError) */
 #define PDA_ERR_DEVICE       -5  /* the HIP device query failed */
@@ -191,7 +192,7 @@ typedef struct pda_shape {
     int32_t num_q_heads;         /* Hq >= 1, multiple of num_kv_heads */
     int32_t num_kv_heads;        /* Hkv >= 1 */
     int32_t head_size;           /* D: 64, 128 or 256 */
-    int32_t block_size;          /* bs >= 1 (any value, e.g. 16 or 784) */
+    int32_t block_size;          /* bs >= 1 (any value, e.g. 16 or 784); bs * D <= INT32_MAX */
     int32_t num_blocks;          /* NB >= 1: blocks in each of k_cache, v_cache */
     int32_t max_blocks_per_seq;  /* MBS >= 1: row length of block_table */
     int32_t max_seq_len;         /* >= every seq_lens[b], <= MBS * bs; sizes the plan */
@@ -283,7 +284,8 @@ int paged_decode_attn_timed(const pda_shape_t* shape, const pda_plan_t* plan,
  *   trace_slot [B][Hkv][max_seq_len]  physical slot  block_id * bs + (t % bs)
  *   trace_part [B][Hkv][max_seq_len]  the partition p that consumed t
  * and for every unit trace_range [B][Hkv][P][2] = (t0, t1) (t1 <= t0 when the
- * partition is empty).  Entries for t >= seq_lens[b], and for t before a
+ * partition is empty).  PDA_ERR_UNSUPPORTED when num_blocks * bs exceeds
+ * INT32_MAX (a slot id would not fit).  Entries for t >= seq_lens[b], and for t before a
  * sliding window, are left untouched.
  * Device pointers; the caller pre-fills them with a sentinel. */
 int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan, int32_t rows,

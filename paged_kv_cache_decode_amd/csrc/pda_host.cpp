@@ -229,6 +229,9 @@ int pda_check_shape(const pda_shape_t* s) {
     if (s->q_len > PDA_MAX_ROWS || rows_of(s) > PDA_MAX_ROWS) return PDA_ERR_UNSUPPORTED;
     if ((int64_t)s->max_seq_len > (int64_t)s->max_blocks_per_seq * s->block_size)
         return PDA_ERR_INVALID;
+    // one (block, KV head) slab of the pool, in elements, is a 32-bit kernel
+    // parameter (the head stride)
+    if ((int64_t)s->block_size * s->head_size > INT32_MAX) return PDA_ERR_UNSUPPORTED;
     if (s->max_seq_len > kMaxSeqLen) return PDA_ERR_UNSUPPORTED;
     if (s->num_seqs > kMaxGridYZ || s->num_kv_heads > kMaxGridYZ ||
         s->num_q_heads > kMaxGridYZ || (int64_t)s->num_seqs * q_len_of(s) > kMaxGridYZ)
@@ -406,6 +409,8 @@ int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl, int32_t 
     if (!block_table || !seq_lens || !trace_slot || !trace_part || !trace_range)
         return PDA_ERR_INVALID;
     if (rows != 0 && rows != 1) return PDA_ERR_INVALID;
+    // the recorded physical slot, block_id * bs + t % bs, is an int32
+    if ((int64_t)s->num_blocks * s->block_size > INT32_MAX) return PDA_ERR_UNSUPPORTED;
     const int pattern = pl->variant == PDA_VARIANT_MFMA ? 1 + rows : 0;
     DecodeParams p = make_params(s, pl, 1.0f);
     p.block_table = block_table;

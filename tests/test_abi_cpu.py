@@ -94,6 +94,9 @@ BAD_SHAPES = [
     (dict(q_len=9), pda.PDA_ERR_UNSUPPORTED),                       # 9 x 4 rows > 32
     (dict(q_len=33, num_q_heads=8), pda.PDA_ERR_UNSUPPORTED),      # 33 rows
     (dict(kv_dtype=2), pda.PDA_ERR_UNSUPPORTED),
+    # block_size * head_size must fit the kernels' 32-bit head stride
+    (dict(block_size=(1 << 23) + 1, head_size=256, max_blocks_per_seq=1, max_seq_len=64),
+     pda.PDA_ERR_UNSUPPORTED),
     (dict(kv_dtype=1, k_scale=0.0, v_scale=1.0), pda.PDA_ERR_INVALID),
     (dict(kv_dtype=1, k_scale=1.0, v_scale=float("inf")), pda.PDA_ERR_INVALID),
     (dict(kv_dtype=1, k_scale=float("nan"), v_scale=1.0), pda.PDA_ERR_INVALID),
