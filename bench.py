@@ -183,6 +183,7 @@ def summary(name, case, r):
             "kernel_GBps": round(kgbs, 1), "kernel_pct_of_peak": round(100 * kgbs / PEAK_GBS, 2),
             "us_per_context_token": round(us / sum(case.seq_lens), 6),
             "variant": {1: "valu", 2: "mfma"}.get(r["plan"].variant, "?"),
+            "merge": {0: "fused", 1: "kernel"}.get(r["plan"].merge, "?"),
             "replica_pools": r["replicas"],
             "passes_us": [round(p["call_ms"] * 1e3, 3) for p in r["passes"]]}
 
@@ -385,7 +386,8 @@ def main():
         "us_per_call": head["us_per_call"],
         "pct_of_peak": head["pct_of_peak"],
         "us_per_context_token": head["us_per_context_token"],
-        "plan": {"P": head["P"], "T_p": head["T_p"], "replica_pools": head["replica_pools"]},
+        "plan": {"P": head["P"], "T_p": head["T_p"], "merge": head["merge"],
+                 "replica_pools": head["replica_pools"]},
         "passes_us": head["passes_us"],
         "roofline": {"bound": "hbm",
                      "kernel": f"decode_{head['variant']}_kernel (split-KV)",

@@ -162,13 +162,18 @@ extern "C" {
  * (PDA_ERR_UNSUPPORTED otherwise).  When P == 1 the main kernel writes `out` directly and no
  * workspace is used; otherwise it writes fp32 partials that are merged with
  * the log-sum-exp rule, either
- *   PDA_MERGE_KERNEL by a separate merge kernel on the same stream (the
- *                    plan's choice: the merge is spread over D/64 x Hq x B
- *                    workgroups), or
  *   PDA_MERGE_FUSED  by the last workgroup of each (b, g) to finish, found
  *                    with an atomic counter in the workspace (one launch;
- *                    that workgroup alone reads P x G x D partials, which
- *                    only pays when that product is small).
+ *                    that workgroup alone reads the unit's P x R x D fp32
+ *                    partials), or
+ *   PDA_MERGE_KERNEL by a separate merge kernel on the same stream (spread
+ *                    over D/64 x Hq x B*q_len workgroups).
+ * The plan picks PDA_MERGE_FUSED when 1 < P <= PDA_FUSED_MAX_PARTS and
+ * P * R * D * 4 <= PDA_FUSED_MAX_BYTES (the last workgroup then reads all of
+ * them in one round of loads, and saving the second launch pays: measured
+ * 1.6-2.8 us per call at 1K-2K tokens), PDA_MERGE_KERNEL otherwise (with
+ * more partitions the fused tail takes more round trips than the merge
+ * kernel's launch costs).
  * The workspace holds partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
  * pairs [B][q_len][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
  * aligned to 256 bytes.  The counters must be zero when a fused call starts;
@@ -186,6 +191,8 @@ extern "C" {
 
 #define PDA_MERGE_FUSED   0
 #define PDA_MERGE_KERNEL  1
+#define PDA_FUSED_MAX_PARTS  16
+#define PDA_FUSED_MAX_BYTES  (32 * 1024)
 
 typedef struct pda_shape {
     int32_t num_seqs;            /* B >= 1 */
@@ -207,7 +214,7 @@ typedef struct pda_plan {
     int32_t num_partitions;        /* P >= 1 */
     int32_t tokens_per_partition;  /* T_p, a positive multiple of PDA_TP_ALIGN */
     int32_t variant;               /* PDA_VARIANT_VALU or PDA_VARIANT_MFMA */
-    int32_t merge;                 /* PDA_MERGE_KERNEL (the plan's choice) or PDA_MERGE_FUSED */
+    int32_t merge;                 /* PDA_MERGE_FUSED or PDA_MERGE_KERNEL (rule above) */
     int32_t cu_count;              /* the C the plan was made for */
     int64_t workspace_bytes;       /* 0 when P == 1 */
 } pda_plan_t;

@@ -22,6 +22,9 @@ WG_MANY_BYTES = 1024 * 1024
 WG_ONE_BYTES = 1024 * 1024
 MAX_PARTITIONS = 65535
 VALU, MFMA = 1, 2
+MERGE_FUSED, MERGE_KERNEL = 0, 1
+FUSED_MAX_PARTS = 16
+FUSED_MAX_BYTES = 32 * 1024
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -72,6 +75,17 @@ def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_
         t_p = max(t_p, _cdiv(_cdiv(lspan, MAX_PARTITIONS), TP_ALIGN) * TP_ALIGN)
     p = max(1, _cdiv(lspan, t_p))
     return p, t_p, var
+
+
+def merge(p: int, rows: int, head_size: int) -> int:
+    """Merge mode: fused (the last workgroup of a unit merges) when the
+    context is split (P > 1) into at most 16 partitions whose fp32 partial
+    outputs, P * R * D * 4 bytes for the unit's R rows, are at most 32 KiB;
+    the separate merge kernel otherwise (and when P == 1, where nothing is
+    merged)."""
+    if 1 < p <= FUSED_MAX_PARTS and p * rows * head_size * 4 <= FUSED_MAX_BYTES:
+        return MERGE_FUSED
+    return MERGE_KERNEL
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,

@@ -267,7 +267,12 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     plan->num_partitions = (int32_t)P;
     plan->tokens_per_partition = (int32_t)tp;
     plan->variant = mfma ? PDA_VARIANT_MFMA : PDA_VARIANT_VALU;
-    plan->merge = PDA_MERGE_KERNEL;
+    // fused merge while the unit's partials are small enough for its last
+    // workgroup to read them in one round of loads
+    plan->merge = P > 1 && P <= PDA_FUSED_MAX_PARTS &&
+                          P * R * s->head_size * 4 <= PDA_FUSED_MAX_BYTES
+                      ? PDA_MERGE_FUSED
+                      : PDA_MERGE_KERNEL;
     plan->cu_count = cu_count;
     plan->workspace_bytes = pda_workspace_bytes(s, plan);
     return PDA_OK;

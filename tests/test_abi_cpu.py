@@ -61,7 +61,7 @@ def test_plan_matches_oracle_plan(D):
         P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n, kv_fp8=f8)
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
         assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv, q_len=n)
-        assert got.merge == pda.PDA_MERGE_KERNEL
+        assert got.merge == oplan.merge(P, n * G, D)
         assert got.cu_count == cu
 
 
@@ -74,8 +74,8 @@ def test_plan_golden_through_library():
                                max(1, -(-c["Lmax"] // 16)), c["Lmax"],
                                sliding_window=c.get("W", 0), q_len=c.get("q_len", 1))
         got = pda.pda_plan_for_cus(shape, g["cu_count"])
-        assert (got.num_partitions, got.tokens_per_partition, got.variant) == \
-            (c["P"], c["T_p"], c["variant"]), c["name"]
+        assert (got.num_partitions, got.tokens_per_partition, got.variant, got.merge) == \
+            (c["P"], c["T_p"], c["variant"], c["merge"]), c["name"]
 
 
 BAD_SHAPES = [

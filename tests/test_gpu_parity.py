@@ -185,10 +185,13 @@ def test_fused_and_kernel_merge_reuse_workspace(mk):
     case = (configs.cfg4(16384, device="cuda") if mk == "cfg4"
             else configs.cfg5(device="cuda", lo=1, hi=5000, cell=2))
     shape = shape_of(case)
-    planned = pda.paged_decode_attn_plan(shape)
-    assert planned.merge == pda.PDA_MERGE_KERNEL and planned.num_partitions > 1
-    kplan = planned
-    planned = plan_of(planned.num_partitions, planned.tokens_per_partition,
+    dplan = pda.paged_decode_attn_plan(shape)
+    assert dplan.num_partitions > 1
+    # the device plan's partitions and variant under each merge mode,
+    # whichever mode the plan picked
+    kplan = plan_of(dplan.num_partitions, dplan.tokens_per_partition, dplan.variant,
+                    merge=pda.PDA_MERGE_KERNEL)
+    planned = plan_of(dplan.num_partitions, dplan.tokens_per_partition, dplan.variant,
                       merge=pda.PDA_MERGE_FUSED)
     ws = torch.empty(pda.pda_workspace_bytes(shape, planned), dtype=torch.uint8, device="cuda")
     pda.paged_decode_attn_workspace_init(ws)

@@ -20,6 +20,8 @@ def test_plan_hand_derived_values():
         P, T, var = plan.partition(c["B"], c["Hkv"], c["G"], c["D"], c["Lmax"], g["cu_count"],
                                    window=c.get("W", 0), q_len=c.get("q_len", 1))
         assert (P, T, var) == (c["P"], c["T_p"], c["variant"]), c["name"]
+        R = c["G"] * c.get("q_len", 1)
+        assert plan.merge(P, R, c["D"]) == c["merge"], c["name"]
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
@@ -48,6 +50,11 @@ def test_plan_invariants(D):
         else:
             assert P == 1
         assert var == plan.MFMA if n * G > 8 else var in (plan.VALU, plan.MFMA)
+        m = plan.merge(P, n * G, D)
+        assert m == plan.MERGE_KERNEL if P == 1 or P > 16 else m in (plan.MERGE_FUSED,
+                                                                       plan.MERGE_KERNEL)
+        if m == plan.MERGE_FUSED:
+            assert P * n * G * D * 4 <= 32 * 1024
 
 
 def test_workspace_bytes():
