@@ -139,6 +139,36 @@ __device__ inline void store_coherent(float* ptr, float v) {
 __device__ inline float load_coherent(const float* ptr) {
     return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A buffer resource over `base`, made wave-uniform with readfirstlane (a
+// lane-varying resource would make the compiler loop over the lanes' distinct
+// values); `base` must be the same for every lane of the wave.
+constexpr int kBufferSc1 = 16;  // cache-policy bit sc1 of a buffer access: device scope
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    // each half through uint32_t: the builtin returns int, and a low half
+    // with bit 31 set would otherwise sign-extend into the high half
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), (short)0,
+                                             0x7fffffff, kBufferWord3);
+}
+// N = 2 or 4 consecutive floats stored at base + off (byte offset, 8N-byte
+// aligned) at device scope in one access: written through to the point where
+// every XCD sees them, like store_coherent, but as one 8- or 16-byte store
+// rather than N 4-byte ones (each of which costs a memory write of its own).
+template <int N>
+__device__ inline void store_coherent_vec(float* base, uint32_t off, const float* v) {
+    static_assert(N == 2 || N == 4, "8- or 16-byte stores");
+    if constexpr (N == 4) {
+        const u32x4_t w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                           __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, uniform_rsrc(base), off, 0, kBufferSc1);
+    } else {
+        const u32x2_t w = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, uniform_rsrc(base), off, 0, kBufferSc1);
+    }
+}
+
 // Wait until this wave's outstanding memory operations (its device-scope
 // stores included) have completed; also a compiler barrier for memory.
 __device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -439,11 +469,28 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
     const int64_t prow = row * p.num_partitions + part;
     float* dst = p.ws_o + prow * D + d0;
     if (p.fused_merge) {  // read back by another workgroup of this launch
+        // offsets from the unit's first row: its partials span R' rows of
+        // P x D floats (R' = R, or more rows apart with q_len > 1)
+        const int64_t row0 = row_index(p, b, g, 0);
+        const int64_t span = (row_index(p, b, g, p.rows - 1) - row0 + 1) * p.num_partitions * D * 4;
+        if (span < ((int64_t)1 << 31)) {
+            const int64_t prel = (row - row0) * p.num_partitions + part;
+            float* obase = p.ws_o + row0 * p.num_partitions * D;
+            const uint32_t off = (uint32_t)((prel * D + d0) * 4);
 #pragma unroll
-        for (int e = 0; e < kDpt; ++e) store_coherent(dst + e, o[e]);
-        if (d0 == 0) {
-            store_coherent(p.ws_ml + prow * 2, M);
-            store_coherent(p.ws_ml + prow * 2 + 1, den);
+            for (int e = 0; e < kDpt; e += (kDpt % 4 == 0 ? 4 : 2))
+                store_coherent_vec<kDpt % 4 == 0 ? 4 : 2>(obase, off + 4 * e, o + e);
+            if (d0 == 0) {
+                const float mlv[2] = {M, den};
+                store_coherent_vec<2>(p.ws_ml + row0 * p.num_partitions * 2, (uint32_t)(prel * 8), mlv);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kDpt; ++e) store_coherent(dst + e, o[e]);
+            if (d0 == 0) {
+                store_coherent(p.ws_ml + prow * 2, M);
+                store_coherent(p.ws_ml + prow * 2 + 1, den);
+            }
         }
     } else {              // read by the merge kernel after this launch
 #pragma unroll
@@ -471,15 +518,7 @@ constexpr int kMergeUnroll = 16;  // partitions whose loads are in flight togeth
 // `base` must be wave-uniform (it is made so: a lane-varying resource would
 // make the compiler loop over the lanes' distinct values).
 __device__ inline float4 load_coherent16(const float* base, uint32_t off) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    // each half through uint32_t: the builtin returns int, and a low half
-    // with bit 31 set would otherwise sign-extend into the high half
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint64_t ua = (hi << 32) | lo;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(ua), (short)0, 0x7fffffff, kBufferWord3);
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 16);  // sc1
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(uniform_rsrc(base), off, 0, kBufferSc1);
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                        __uint_as_float(v.w));
 }
