@@ -115,9 +115,16 @@ hipError_t launch_zero_fill(void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
                         hipStream_t stream);
 
-// Bytes of dynamic LDS the MFMA kernel uses (head chunks of kHeadChunk).
+// Rows the MFMA kernel stages in LDS at once at the end of a unit: 16 (a
+// whole 16-row matrix-core chunk, one barrier) up to head size 128, 8 at 256
+// (LDS).
+__host__ __device__ constexpr int mfma_row_chunk(int head_size) {
+    return head_size <= 128 ? 16 : kHeadChunk;
+}
+
+// Bytes of dynamic LDS the MFMA kernel uses (rows staged mfma_row_chunk at a time).
 inline size_t mfma_lds_bytes(int head_size, int tbl_capacity) {
-    return (size_t)kWaves * kHeadChunk * (head_size + 2) * sizeof(float) +
+    return (size_t)kWaves * mfma_row_chunk(head_size) * (head_size + 2) * sizeof(float) +
            (size_t)tbl_capacity * sizeof(int32_t);
 }
 

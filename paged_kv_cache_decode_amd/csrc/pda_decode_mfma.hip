@@ -129,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     using VRaw = typename std::conditional<F8, uint2, uint4>::type;  // 8 V elements
     extern __shared__ float smem[];
     float* red = smem;                                                       // [kWaves][8][D+2]
-    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * kHeadChunk * (D + 2));
+    constexpr int HC = mfma_row_chunk(D);  // rows staged in LDS at a time
+    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * HC * (D + 2));
 
     // grid (Hkv, B, P): the partition index varies slowest (see the launcher)
     const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
@@ -427,13 +428,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
 
     // merge the wavefronts and write the unit's result, rows in chunks
-    for (int h0 = 0; h0 < R; h0 += kHeadChunk) {
-        const int hn = min(kHeadChunk, R - h0);
+    for (int h0 = 0; h0 < R; h0 += HC) {
+        const int hn = min(HC, R - h0);
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             const int hi = 16 * c + c16 - h0;
             if (hi < 0 || hi >= hn) continue;
-            float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+            float* row = red + (wave * HC + hi) * (D + 2);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (4 * q4 + i >= CW) continue;  // repeated d-rows (D = 64)
@@ -449,14 +450,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             for (int c = 0; c < RC; ++c) {
                 const int hi = 16 * c + c16 - h0;
                 if (hi < 0 || hi >= hn) continue;
-                float* row = red + (wave * kHeadChunk + hi) * (D + 2);
+                float* row = red + (wave * HC + hi) * (D + 2);
                 row[D] = m[c];
                 row[D + 1] = l[c];
             }
         }
         __syncthreads();
-        write_unit_rows<Elt, D>(p, red, kHeadChunk, h0, hn, b, g, part);
-        if (h0 + kHeadChunk < R) __syncthreads();  // before the next chunk reuses red
+        // the combine takes kHeadChunk rows per pass (one row per 32 threads)
+        for (int r0 = 0; r0 < hn; r0 += kHeadChunk)
+            write_unit_rows<Elt, D>(p, red + r0 * (D + 2), HC, h0 + r0, min(kHeadChunk, hn - r0), b,
+                                    g, part);
+        if (h0 + HC < R) __syncthreads();  // before the next chunk reuses red
     }
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
