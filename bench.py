@@ -267,12 +267,30 @@ def cpu_baseline(case, seconds):
         t += time.perf_counter() - t0
         n += 1
     per_call = t / n
+    # the same call on one thread, over a bounded share of the budget
+    n1, t1 = 0, 0.0
+    while t1 < seconds / 4 or n1 == 0:
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, lens, case.scale, nthreads=1, window=case.sliding_window)
+        t1 += time.perf_counter() - t0
+        n1 += 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return ref, {"value": round(case.kv_bytes() / per_call / 1e9, 3), "unit": "GB/s",
                  "cores": threads, "kind": "oracle",
                  "us_per_call": round(per_call * 1e6, 1),
                  "sample": f"{n} full decode call(s) of the headline workload "
                            f"({case.B}x{case.Hq} rows over {sum(case.seq_lens)} tokens), "
-                           f"{t:.1f} s of CPU time, OpenMP over rows"}
+                           f"{t:.1f} s of CPU time, OpenMP over rows",
+                 "single_thread": {"value": round(case.kv_bytes() / (t1 / n1) / 1e9, 3),
+                                   "unit": "GB/s", "us_per_call": round(t1 / n1 * 1e6, 1),
+                                   "sample": f"{n1} call(s), {t1:.1f} s"},
+                 "cpu_model": model}
 
 
 def main():
