@@ -168,18 +168,22 @@ extern "C" {
  *                    partials), or
  *   PDA_MERGE_KERNEL by a separate merge kernel on the same stream (spread
  *                    over D/64 x Hq x B*q_len workgroups).
- * The plan picks PDA_MERGE_FUSED when 1 < P <= PDA_FUSED_MAX_PARTS and
- * P * R * D * 4 <= PDA_FUSED_MAX_BYTES (the last workgroup then reads all of
+ * The plan picks PDA_MERGE_FUSED when 1 < P <= PDA_FUSED_MAX_PARTS,
+ * B * Hkv <= PDA_FUSED_MAX_UNITS and P * R * D * 4 <= PDA_FUSED_MAX_BYTES
+ * (the last workgroup then reads all of
  * them in one round of loads, and saving the second launch pays: measured
  * 1.6-2.8 us per call at 1K-2K tokens), PDA_MERGE_KERNEL otherwise (with
  * more partitions the fused tail takes more round trips than the merge
  * kernel's launch costs).
- * The workspace holds partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
- * pairs [B][q_len][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
- * aligned to 256 bytes.  The counters must be zero when a fused call starts;
- * every fused call leaves them zero again, so a workspace needs zeroing once
- * (paged_decode_attn_workspace_init, or any zero fill) before its first use.
- * Calls that run concurrently need separate workspaces. */
+ * The workspace (P > 1) holds PDA_FUSED_MAX_UNITS int32 arrival counters
+ * first (unit (b, g) uses entry b * Hkv + g), then partial outputs
+ * [B][q_len][Hq][P][D] fp32, then (m, l) pairs [B][q_len][Hq][P][2] fp32,
+ * each part aligned to 256 bytes.  The counters must be zero when a fused
+ * call starts; every fused call leaves them zero again, and they sit at the
+ * same place for every shape, so a workspace zeroed once
+ * (paged_decode_attn_workspace_init, or any zero fill) before its first use
+ * serves any sequence of calls, of any shapes and either merge, that it is
+ * large enough for.  Calls that run concurrently need separate workspaces. */
 #define PDA_TILE            16
 #define PDA_TP_ALIGN        64
 #define PDA_MFMA_MIN_GROUP  2
@@ -193,6 +197,7 @@ extern "C" {
 #define PDA_MERGE_KERNEL  1
 #define PDA_FUSED_MAX_PARTS  16
 #define PDA_FUSED_MAX_BYTES  (32 * 1024)
+#define PDA_FUSED_MAX_UNITS  16384
 
 typedef struct pda_shape {
     int32_t num_seqs;            /* B >= 1 */

@@ -25,6 +25,7 @@ VALU, MFMA = 1, 2
 MERGE_FUSED, MERGE_KERNEL = 0, 1
 FUSED_MAX_PARTS = 16
 FUSED_MAX_BYTES = 32 * 1024
+FUSED_MAX_UNITS = 16384
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -77,28 +78,32 @@ def partition(num_seqs: int, num_kv_heads: int, group: int, head_size: int, max_
     return p, t_p, var
 
 
-def merge(p: int, rows: int, head_size: int) -> int:
+def merge(p: int, rows: int, head_size: int, units: int = 1) -> int:
     """Merge mode: fused (the last workgroup of a unit merges) when the
     context is split (P > 1) into at most 16 partitions whose fp32 partial
-    outputs, P * R * D * 4 bytes for the unit's R rows, are at most 32 KiB;
-    the separate merge kernel otherwise (and when P == 1, where nothing is
+    outputs, P * R * D * 4 bytes for the unit's R rows, are at most 32 KiB,
+    and the B * Hkv units fit the workspace's 16384 arrival counters; the
+    separate merge kernel otherwise (and when P == 1, where nothing is
     merged)."""
-    if 1 < p <= FUSED_MAX_PARTS and p * rows * head_size * 4 <= FUSED_MAX_BYTES:
+    if (1 < p <= FUSED_MAX_PARTS and units <= FUSED_MAX_UNITS
+            and p * rows * head_size * 4 <= FUSED_MAX_BYTES):
         return MERGE_FUSED
     return MERGE_KERNEL
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,
                     num_kv_heads: int = 1, q_len: int = 1) -> int:
-    """Partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
-    [B][q_len][Hq][P][2] fp32, then arrival counters [B][Hkv] int32, each part
-    rounded up to 256 bytes; none when P == 1."""
+    """16384 int32 arrival counters (a fixed block, the same for every
+    shape), then partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
+    [B][q_len][Hq][P][2] fp32, each part rounded up to 256 bytes; none when
+    P == 1.  (num_kv_heads no longer changes the size: the counter block is
+    fixed.)"""
     if p <= 1:
         return 0
 
     def r256(x):
         return _cdiv(x, 256) * 256
     rows = num_seqs * max(1, q_len) * num_q_heads
-    return (r256(rows * p * head_size * 4)
-            + r256(rows * p * 2 * 4)
-            + r256(num_seqs * num_kv_heads * 4))
+    return (FUSED_MAX_UNITS * 4
+            + r256(rows * p * head_size * 4)
+            + r256(rows * p * 2 * 4))

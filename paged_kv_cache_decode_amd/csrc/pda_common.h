@@ -64,7 +64,7 @@ struct DecodeParams {
     void* out;                 // [B][q_len][Hq][D]
     float* ws_o;               // [B][q_len][Hq][P][D]    (P > 1 only)
     float* ws_ml;              // [B][q_len][Hq][P][2]    (P > 1 only)
-    int32_t* counters;         // [B][Hkv] arrival counters (fused merge)
+    int32_t* counters;         // arrival counters (fused merge), entry b * Hkv + g
     int32_t* trace_slot;       // trace kernel only
     int32_t* trace_part;
     int32_t* trace_range;

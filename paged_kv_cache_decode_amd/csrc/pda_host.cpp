@@ -112,6 +112,9 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool kv_fp8(const pda_shape_t* s) { return s->kv_dtype == PDA_KV_FP8_E4M3; }
 int64_t round256(int64_t x) { return cdiv64(x, 256) * 256; }
+// the fixed block of arrival counters at the start of a workspace
+constexpr int64_t kCounterBytes = (int64_t)PDA_FUSED_MAX_UNITS * 4;
+static_assert(kCounterBytes % 256 == 0, "the partials after the counters stay 256-byte aligned");
 
 // block sizes that are multiples of 16 tokens take the one-lookup-per-round
 // path of the kernels (kAlignTokens)
@@ -148,6 +151,10 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
         pl->num_partitions > kMaxGridYZ)
         return PDA_ERR_UNSUPPORTED;
     if (pl->merge != PDA_MERGE_FUSED && pl->merge != PDA_MERGE_KERNEL) return PDA_ERR_INVALID;
+    // the fused merge counts arrivals in the workspace's fixed counter block
+    if (pl->merge == PDA_MERGE_FUSED && pl->num_partitions > 1 &&
+        (int64_t)s->num_seqs * s->num_kv_heads > PDA_FUSED_MAX_UNITS)
+        return PDA_ERR_UNSUPPORTED;
     const int R = (int)rows_of(s);
     if (pl->variant == PDA_VARIANT_VALU) {
         if (R > kValuMaxGroup || kv_fp8(s)) return PDA_ERR_UNSUPPORTED;
@@ -269,7 +276,7 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     plan->variant = mfma ? PDA_VARIANT_MFMA : PDA_VARIANT_VALU;
     // fused merge while the unit's partials are small enough for its last
     // workgroup to read them in one round of loads
-    plan->merge = P > 1 && P <= PDA_FUSED_MAX_PARTS &&
+    plan->merge = P > 1 && P <= PDA_FUSED_MAX_PARTS && units <= PDA_FUSED_MAX_UNITS &&
                           P * R * s->head_size * 4 <= PDA_FUSED_MAX_BYTES
                       ? PDA_MERGE_FUSED
                       : PDA_MERGE_KERNEL;
@@ -282,8 +289,7 @@ int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
     if (!s || !pl) return PDA_ERR_INVALID;
     if (pl->num_partitions <= 1) return 0;
     const int64_t rows = (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
-    return round256(rows * s->head_size * 4) + round256(rows * 2 * 4) +
-           round256((int64_t)s->num_seqs * s->num_kv_heads * 4);
+    return kCounterBytes + round256(rows * s->head_size * 4) + round256(rows * 2 * 4);
 }
 
 int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream) {
@@ -335,10 +341,9 @@ static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
             (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
         char* ws = static_cast<char*>(workspace);
         const int64_t o_bytes = round256(rows * s->head_size * 4);
-        const int64_t ml_bytes = round256(rows * 2 * 4);
-        p.ws_o = reinterpret_cast<float*>(ws);
-        p.ws_ml = reinterpret_cast<float*>(ws + o_bytes);
-        p.counters = reinterpret_cast<int32_t*>(ws + o_bytes + ml_bytes);
+        p.counters = reinterpret_cast<int32_t*>(ws);
+        p.ws_o = reinterpret_cast<float*>(ws + kCounterBytes);
+        p.ws_ml = reinterpret_cast<float*>(ws + kCounterBytes + o_bytes);
         p.fused_merge = pl->merge == PDA_MERGE_FUSED;
     }
     // more than two workgroups per CU in all: at most two resident at a time

@@ -61,7 +61,7 @@ def test_plan_matches_oracle_plan(D):
         P, T, var = oplan.partition(B, Hkv, G, D, L, cu, window=W, q_len=n, kv_fp8=f8)
         assert (got.num_partitions, got.tokens_per_partition, got.variant) == (P, T, var)
         assert got.workspace_bytes == oplan.workspace_bytes(B, Hkv * G, D, P, Hkv, q_len=n)
-        assert got.merge == oplan.merge(P, n * G, D)
+        assert got.merge == oplan.merge(P, n * G, D, B * Hkv)
         assert got.cu_count == cu
 
 
@@ -220,3 +220,21 @@ def test_plan_caps_partitions_at_the_grid_limit():
     rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(bad), 1, 1, 1, 1, 1,
                                          1.0, 1, 1, 1 << 40, None)
     assert rc == pda.PDA_ERR_UNSUPPORTED
+
+
+def test_forced_fused_merge_beyond_the_counter_block_is_refused():
+    """A fused merge counts arrivals in the workspace's fixed block of 16384
+    counters: a forced fused plan for more units is refused before launch."""
+    lib = pda.load_library()
+    shape = _shape(num_seqs=2049, num_kv_heads=8, num_q_heads=32, max_blocks_per_seq=4,
+                   max_seq_len=64)  # 16392 units
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    for merge, status in ((pda.PDA_MERGE_FUSED, pda.PDA_ERR_UNSUPPORTED),):
+        plan = pda.PdaPlan(num_partitions=2, tokens_per_partition=64, variant=pda.PDA_VARIANT_MFMA,
+                           merge=merge, cu_count=0, workspace_bytes=0)
+        rc = lib.paged_decode_attn_with_plan(ctypes.byref(shape), ctypes.byref(plan), fake, fake,
+                                             fake, fake, fake, 1.0, fake, fake, 1 << 40, None)
+        assert rc == status
+    # the device-independent plan never picks it there
+    got = pda.pda_plan_for_cus(shape, 256)
+    assert got.num_partitions == 1 or got.merge == pda.PDA_MERGE_KERNEL

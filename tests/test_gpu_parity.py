@@ -209,11 +209,38 @@ def test_fused_and_kernel_merge_reuse_workspace(mk):
                 first = bits(out)
             else:
                 assert np.array_equal(first, bits(out))
-    # the counters (last part of the workspace) are back at zero
-    nctr = case.B * case.Hkv
-    ctr_bytes = -(-(nctr * 4) // 256) * 256
-    ctr = ws[ws.numel() - ctr_bytes:].view(torch.int32)[:nctr]
+    # the counters (the fixed block at the start of the workspace) are back at zero
+    ctr = ws[:16384 * 4].view(torch.int32)
     assert int(ctr.abs().sum().item()) == 0
+
+
+def test_one_workspace_serves_a_sequence_of_shapes():
+    """Zeroed once, one workspace serves calls of different shapes under the
+    device plan, fused merge and merge kernel alike: the arrival counters sit
+    in a fixed block at its start, where no shape's partials land, and each
+    fused call leaves them zero.  Every call matches the oracle and equals
+    the same call on a fresh workspace bit for bit."""
+    cases = [configs.cfg2(32, 1024, device="cuda"),         # fused, 8 partitions
+             configs.cfg3(8, 1024, device="cuda"),          # fused, 128 units
+             configs.cfg2(32, 4096, device="cuda"),         # merge kernel, 32 partitions
+             configs.cfg3(1, 2048, device="cuda", cell=3),  # fused, 16 partitions
+             configs.cfg2(32, 1024, device="cuda")]         # the first shape again
+    need = max(pda.paged_decode_attn_workspace_size(shape_of(c)) for c in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    pda.paged_decode_attn_workspace_init(ws)
+    merges = set()
+    for case in cases:
+        merges.add(pda.paged_decode_attn_plan(shape_of(case)).merge)
+        out = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                    case.seq_lens_t, case.scale, workspace=ws,
+                                    max_seq_len=case.max_seq_len)
+        fresh = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                      case.seq_lens_t, case.scale, max_seq_len=case.max_seq_len)
+        torch.cuda.synchronize()
+        check(case, out, per_seq=True)
+        assert np.array_equal(bits(out), bits(fresh))
+    assert merges == {pda.PDA_MERGE_FUSED, pda.PDA_MERGE_KERNEL}
+    assert int(ws[:16384 * 4].view(torch.int32).abs().sum().item()) == 0
 
 
 def test_edge_lengths():

@@ -21,7 +21,7 @@ def test_plan_hand_derived_values():
                                    window=c.get("W", 0), q_len=c.get("q_len", 1))
         assert (P, T, var) == (c["P"], c["T_p"], c["variant"]), c["name"]
         R = c["G"] * c.get("q_len", 1)
-        assert plan.merge(P, R, c["D"]) == c["merge"], c["name"]
+        assert plan.merge(P, R, c["D"], c["B"] * c["Hkv"]) == c["merge"], c["name"]
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
@@ -50,7 +50,7 @@ def test_plan_invariants(D):
         else:
             assert P == 1
         assert var == plan.MFMA if n * G > 8 else var in (plan.VALU, plan.MFMA)
-        m = plan.merge(P, n * G, D)
+        m = plan.merge(P, n * G, D, B * Hkv)
         assert m == plan.MERGE_KERNEL if P == 1 or P > 16 else m in (plan.MERGE_FUSED,
                                                                        plan.MERGE_KERNEL)
         if m == plan.MERGE_FUSED:
@@ -58,11 +58,19 @@ def test_plan_invariants(D):
 
 
 def test_workspace_bytes():
+    counters = 16384 * 4  # the fixed block of arrival counters, first
     assert plan.workspace_bytes(1, 32, 128, 1) == 0
-    assert plan.workspace_bytes(1, 24, 256, 128, 4) == 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4 + 256
+    assert plan.workspace_bytes(1, 24, 256, 128, 4) == \
+        counters + 24 * 128 * 256 * 4 + 24 * 128 * 2 * 4
     # q_len rows per sequence: q_len times the partial rows
     assert plan.workspace_bytes(2, 8, 64, 3, 2, q_len=4) == \
-        2 * 4 * 8 * 3 * 64 * 4 + 2 * 4 * 8 * 3 * 2 * 4 + 256
+        counters + 2 * 4 * 8 * 3 * 64 * 4 + 2 * 4 * 8 * 3 * 2 * 4
+
+
+def test_fused_merge_needs_the_units_to_fit_the_counter_block():
+    # 16 partitions of 2 rows at D 128: 16 KiB of partials, fused up to 16384 units
+    assert plan.merge(16, 2, 128, 16384) == plan.MERGE_FUSED
+    assert plan.merge(16, 2, 128, 16385) == plan.MERGE_KERNEL
 
 
 def test_expected_trace_matches_token_loop():
