@@ -96,8 +96,8 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, head_size: int, p: int,
     """16384 int32 arrival counters (a fixed block, the same for every
     shape), then partial outputs [B][q_len][Hq][P][D] fp32, then (m, l)
     [B][q_len][Hq][P][2] fp32, each part rounded up to 256 bytes; none when
-    P == 1.  (num_kv_heads no longer changes the size: the counter block is
-    fixed.)"""
+    P == 1.  num_kv_heads does not change the size: the counter block is
+    fixed."""
     if p <= 1:
         return 0
 
