@@ -23,14 +23,65 @@ def shape_of(case: kvgen.Case) -> pda.PdaShape:
     return pda.make_shape(**d)
 
 
+GUARD_BYTES = 4096          # canary bytes on each side of `out` and the workspace
+_CANARY_SEED = 0x5EED
+
+
+def _guarded(nbytes: int, device) -> tuple:
+    """A device buffer of nbytes with GUARD_BYTES of seeded random canary
+    bytes on each side; returns (whole buffer, inner slice, canary copy).
+    The inner slice starts 4096-byte aligned, as a fresh allocation would."""
+    gen = torch.Generator()
+    gen.manual_seed(_CANARY_SEED + nbytes)
+    whole = torch.randint(0, 256, (2 * GUARD_BYTES + max(nbytes, 0),), dtype=torch.uint8,
+                          generator=gen).to(device)
+    return whole, whole[GUARD_BYTES:GUARD_BYTES + nbytes], whole.clone()
+
+
+def _check_guards(name: str, whole: torch.Tensor, before: torch.Tensor, nbytes: int):
+    """The canary bytes on both sides of a guarded buffer are untouched."""
+    for lo, hi, side in ((0, GUARD_BYTES, "before"),
+                         (GUARD_BYTES + nbytes, 2 * GUARD_BYTES + nbytes, "after")):
+        changed = int((whole[lo:hi] != before[lo:hi]).sum().item())
+        assert changed == 0, f"{changed} canary bytes {side} `{name}` were overwritten"
+
+
 def run(case: kvgen.Case, plan=None, out=None) -> torch.Tensor:
+    """One decode call through the C ABI.  `out` and the workspace are carved
+    out of larger buffers whose canary bytes on either side must survive the
+    call (an out-of-bounds store by the decode, the fused merge or the merge
+    kernel shows up here), and the fused merge's arrival counters must be
+    back at zero afterwards."""
+    shape = shape_of(case)
+    need = (pda.paged_decode_attn_workspace_size(shape) if plan is None
+            else pda.pda_workspace_bytes(shape, plan))
+    dev = case.q.device
+    guards = []
+    if out is None:
+        nb = case.q.numel() * case.q.element_size()
+        whole, inner, before = _guarded(nb, dev)
+        out = inner.view(case.q.dtype).view(case.q.shape)
+        guards.append(("out", whole, before, nb))
+    ws = None
+    if need > 0:
+        whole, ws, _ = _guarded(need, dev)
+        ws.zero_()  # the state a workspace starts in (the counters must be zero)
+        guards.append(("workspace", whole, whole.clone(), need))
     out = pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
-                                case.seq_lens_t, case.scale, out=out,
+                                case.seq_lens_t, case.scale, out=out, workspace=ws,
                                 max_seq_len=case.max_seq_len, plan=plan,
                                 sliding_window=case.sliding_window, k_scale=case.k_scale,
                                 v_scale=case.v_scale)
     torch.cuda.synchronize()
+    for g in guards:
+        _check_guards(*g)
+    if ws is not None:
+        ctr = ws[:COUNTER_BYTES].view(torch.int32)
+        assert int(ctr.abs().sum().item()) == 0, "arrival counters left non-zero"
     return out
+
+
+COUNTER_BYTES = 16384 * 4   # the workspace's fixed block of arrival counters
 
 
 def reference(case: kvgen.Case, seqs=None) -> np.ndarray:
@@ -47,11 +98,13 @@ def check(case: kvgen.Case, got: torch.Tensor, ref: np.ndarray = None, seqs=None
     """rel-L-inf of the GPU output against the oracle, NaN-freedom, and
     (optionally) the same score per sequence."""
     g = got.float().cpu().numpy()
+    # NaN-freedom over the whole output, before any subset is scored
+    bad = int(np.count_nonzero(~np.isfinite(g)))
+    assert bad == 0, f"{bad} non-finite values in the GPU output"
     if seqs is not None:
         g = g[list(seqs)]
     if ref is None:
         ref = reference(case, seqs)
-    assert np.all(np.isfinite(g)), "non-finite value in the GPU output"
     err = oracle.rel_linf(g, ref)
     tol = TOL[case.dtype]
     assert err <= tol, f"rel-Linf {err:.3e} > {tol:.1e}"

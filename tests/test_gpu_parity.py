@@ -80,8 +80,7 @@ def test_cfg3_b1_fault_matrix(dtype, L, variant):
 def test_cfg3_b8(dtype, L):
     case = configs.cfg3(8, L, dtype=dtype, device="cuda")
     got = run(case)
-    seqs = [0, 5, 7]
-    check(case, got, seqs=seqs, per_seq=True)
+    check(case, got, per_seq=True)
     clean = kvgen.page(case, "zero", "zero")
     assert np.array_equal(bits(got), bits(run(clean)))
 
@@ -101,10 +100,14 @@ def test_cfg4_low_parallelism(L):
 
 # ---- config 5: batched mixed lengths ------------------------------------
 def test_cfg5_mixed_batch_full_size():
+    """All 64 sequences (1.2M tokens, NaN tails) scored against the oracle,
+    each at the tolerance, and the poisoned run bit-identical to the same
+    content with zero tails."""
     case = configs.cfg5(device="cuda")
     got = run(case)
-    seqs = [0, 1, 17, 31, 42, 63]
-    check(case, got, seqs=seqs, per_seq=True)
+    check(case, got, per_seq=True)
+    clean = kvgen.page(case, "zero", "zero")
+    assert np.array_equal(bits(got), bits(run(clean)))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -142,8 +145,7 @@ def test_mfma_variant_full_size(mk):
             "cfg2-32K": lambda: configs.cfg2(32, 32768, device="cuda"),
             "cfg5": lambda: configs.cfg5(device="cuda")}[mk]()
     got = run(case, plan=device_plan(case, "mfma"))
-    seqs = [0] if case.B == 1 else [0, 9, 33, 63]
-    check(case, got, seqs=seqs, per_seq=True)
+    check(case, got, per_seq=True)
 
 
 def test_mfma_matches_valu_closely():
@@ -372,5 +374,4 @@ def test_tp_share_cfg4_12_2(L, variant):
 def test_tp_share_cfg3_16_8(B, L, variant):
     case = configs.cfg3_tp2(B, L, device="cuda")
     got = run(case, plan=device_plan(case, variant))
-    seqs = None if B == 1 else [0, 5, 7]
-    check(case, got, seqs=seqs, per_seq=True)
+    check(case, got, per_seq=True)

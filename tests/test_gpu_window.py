@@ -151,8 +151,7 @@ def test_sliding_layer_full_size(B, L, variant):
     plan = pda.paged_decode_attn_plan(shape_of(case))
     plan.variant = VARIANTS[variant]
     got = run(case, plan=plan)
-    seqs = [0] if B == 1 else [0, 3, 7]
-    check(case, got, seqs=seqs, per_seq=True)
+    check(case, got, per_seq=True)
     # the window makes a large difference once it cuts most of the context
     if L >= 2 * case.sliding_window:
         q, k, v, lens = kvgen.oracle_inputs(case, [0])
