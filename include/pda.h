@@ -239,7 +239,9 @@ int paged_decode_attn_plan(const pda_shape_t* shape, pda_plan_t* plan);
  * plan has a single partition).  Returns a negative status on error. */
 int64_t paged_decode_attn_workspace_size(const pda_shape_t* shape);
 
-/* Workspace bytes a given plan needs (0 when plan->num_partitions == 1). */
+/* Workspace bytes a given plan needs (0 when plan->num_partitions == 1), or
+ * a negative status for an invalid shape (as pda_check_shape) or a partition
+ * count outside [1, 65535]. */
 int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
 
 /* Zero `bytes` of a device workspace on `stream` (asynchronously): the state

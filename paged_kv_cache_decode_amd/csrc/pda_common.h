@@ -115,6 +115,15 @@ hipError_t launch_zero_fill(void* dst, int64_t bytes, hipStream_t stream);
 hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
                         hipStream_t stream);
 
+// The decode step behind every decode entry point: validates the shape and
+// plan, lays the plan's workspace out in `workspace` (workspace_bytes long),
+// launches the split-KV kernel (with the optional events around it) and the
+// merge kernel when the plan needs one.  Returns a PDA_* status.
+int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q, const void* k_cache,
+               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+               float scale, void* out, void* workspace, int64_t workspace_bytes, void* stream,
+               hipEvent_t ev0, hipEvent_t ev1);
+
 // Rows the MFMA kernel stages in LDS at once at the end of a unit: 16 (a
 // whole 16-row matrix-core chunk, one barrier) up to head size 128, 8 at 256
 // (LDS).

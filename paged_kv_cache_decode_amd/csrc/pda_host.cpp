@@ -212,6 +212,59 @@ DecodeParams make_params(const pda_shape_t* s, const pda_plan_t* pl, float scale
 }
 
 }  // namespace
+
+int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float scale, void* out, void* workspace,
+                      int64_t workspace_bytes, void* stream, hipEvent_t ev0, hipEvent_t ev1) {
+    int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    rc = check_plan(s, pl);
+    if (rc != PDA_OK) return rc;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PDA_ERR_INVALID;
+    const int64_t need = pda_workspace_bytes(s, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PDA_ERR_WORKSPACE;
+
+    DecodeParams p = make_params(s, pl, scale);
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_table = block_table;
+    p.seq_lens = seq_lens;
+    p.out = out;
+    if (need > 0) {
+        const int64_t rows =
+            (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
+        char* ws = static_cast<char*>(workspace);
+        const int64_t o_bytes = round256(rows * s->head_size * 4);
+        p.counters = reinterpret_cast<int32_t*>(ws);
+        p.ws_o = reinterpret_cast<float*>(ws + kCounterBytes);
+        p.ws_ml = reinterpret_cast<float*>(ws + kCounterBytes + o_bytes);
+        p.fused_merge = pl->merge == PDA_MERGE_FUSED;
+    }
+    // more than two workgroups per CU in all: at most two resident at a time
+    int32_t cu = 0;
+    const int64_t wgs = (int64_t)pl->num_partitions * s->num_kv_heads * s->num_seqs;
+    if (device_cu_count(&cu) == PDA_OK && wgs > 2 * (int64_t)cu) p.lds_floor = kLdsTwoPerCu;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool aligned = block_aligned(s);
+    hipError_t e;
+    if (pl->variant == PDA_VARIANT_MFMA)
+        e = kv_fp8(s) ? launch_decode_mfma_fp8(s->dtype, s->head_size, aligned, p, s->num_seqs,
+                                               st, ev0, ev1)
+                      : launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
+                                           ev0, ev1);
+    else
+        e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(p.rows), aligned, p,
+                               s->num_seqs, st, ev0, ev1);
+    if (e != hipSuccess) return PDA_ERR_LAUNCH;
+    if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
+        e = launch_merge(s->dtype, s->head_size, p, (int)(s->num_seqs * q_len_of(s)), st);
+        if (e != hipSuccess) return PDA_ERR_LAUNCH;
+    }
+    return PDA_OK;
+}
+
 }  // namespace pda
 
 using namespace pda;
@@ -287,7 +340,13 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
 
 int64_t pda_workspace_bytes(const pda_shape_t* s, const pda_plan_t* pl) {
     if (!s || !pl) return PDA_ERR_INVALID;
-    if (pl->num_partitions <= 1) return 0;
+    const int rc = pda_check_shape(s);
+    if (rc != PDA_OK) return rc;
+    // a valid shape has B * q_len <= 65535 and Hq <= 65535, so with at most
+    // 65535 partitions the byte count below stays far inside int64
+    if (pl->num_partitions < 1) return PDA_ERR_INVALID;
+    if (pl->num_partitions > kMaxGridYZ) return PDA_ERR_UNSUPPORTED;
+    if (pl->num_partitions == 1) return 0;
     const int64_t rows = (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
     return kCounterBytes + round256(rows * s->head_size * 4) + round256(rows * 2 * 4);
 }
@@ -315,58 +374,6 @@ int64_t paged_decode_attn_workspace_size(const pda_shape_t* s) {
     int rc = paged_decode_attn_plan(s, &pl);
     if (rc != PDA_OK) return rc;
     return pl.workspace_bytes;
-}
-
-static int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
-                      const void* k_cache, const void* v_cache, const int32_t* block_table,
-                      const int32_t* seq_lens, float scale, void* out, void* workspace,
-                      int64_t workspace_bytes, void* stream, hipEvent_t ev0, hipEvent_t ev1) {
-    int rc = pda_check_shape(s);
-    if (rc != PDA_OK) return rc;
-    rc = check_plan(s, pl);
-    if (rc != PDA_OK) return rc;
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return PDA_ERR_INVALID;
-    const int64_t need = pda_workspace_bytes(s, pl);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return PDA_ERR_WORKSPACE;
-
-    DecodeParams p = make_params(s, pl, scale);
-    p.q = q;
-    p.k_cache = k_cache;
-    p.v_cache = v_cache;
-    p.block_table = block_table;
-    p.seq_lens = seq_lens;
-    p.out = out;
-    if (need > 0) {
-        const int64_t rows =
-            (int64_t)s->num_seqs * q_len_of(s) * s->num_q_heads * pl->num_partitions;
-        char* ws = static_cast<char*>(workspace);
-        const int64_t o_bytes = round256(rows * s->head_size * 4);
-        p.counters = reinterpret_cast<int32_t*>(ws);
-        p.ws_o = reinterpret_cast<float*>(ws + kCounterBytes);
-        p.ws_ml = reinterpret_cast<float*>(ws + kCounterBytes + o_bytes);
-        p.fused_merge = pl->merge == PDA_MERGE_FUSED;
-    }
-    // more than two workgroups per CU in all: at most two resident at a time
-    int32_t cu = 0;
-    const int64_t wgs = (int64_t)pl->num_partitions * s->num_kv_heads * s->num_seqs;
-    if (device_cu_count(&cu) == PDA_OK && wgs > 2 * (int64_t)cu) p.lds_floor = kLdsTwoPerCu;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool aligned = block_aligned(s);
-    hipError_t e;
-    if (pl->variant == PDA_VARIANT_MFMA)
-        e = kv_fp8(s) ? launch_decode_mfma_fp8(s->dtype, s->head_size, aligned, p, s->num_seqs,
-                                               st, ev0, ev1)
-                      : launch_decode_mfma(s->dtype, s->head_size, aligned, p, s->num_seqs, st,
-                                           ev0, ev1);
-    else
-        e = launch_decode_valu(s->dtype, s->head_size, valu_group_pad(p.rows), aligned, p,
-                               s->num_seqs, st, ev0, ev1);
-    if (e != hipSuccess) return PDA_ERR_LAUNCH;
-    if (pl->num_partitions > 1 && pl->merge == PDA_MERGE_KERNEL) {
-        e = launch_merge(s->dtype, s->head_size, p, (int)(s->num_seqs * q_len_of(s)), st);
-        if (e != hipSuccess) return PDA_ERR_LAUNCH;
-    }
-    return PDA_OK;
 }
 
 int paged_decode_attn_with_plan(const pda_shape_t* s, const pda_plan_t* pl, const void* q,
