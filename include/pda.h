@@ -319,6 +319,27 @@ int paged_decode_attn_trace(const pda_shape_t* shape, const pda_plan_t* plan, in
  * bad size or 0 / more than 2^20 workgroups. */
 int pda_read_probe(const void* src, int64_t bytes, void* sink, int32_t workgroups, void* stream);
 
+/* The decode step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, layouts, plan and results are those of
+ * paged_decode_attn (the same kernels under the device's own plan, bit-
+ * identical output); the workspace is not an argument: the library keeps one
+ * static device array of PDA_NOALLOC_MAX_WORKSPACE bytes per GPU (held until
+ * the process ends) and uses it as the workspace.  The call allocates
+ * nothing.  Its first call on a device resolves the array's address and
+ * zeroes its counter block with a fill kernel on `stream`; every completed
+ * call leaves the counters zero again.
+ *  - PDA_ERR_WORKSPACE when the plan's workspace exceeds
+ *    PDA_NOALLOC_MAX_WORKSPACE (nothing is launched);
+ *  - every call on one GPU shares that GPU's array: calls that overlap on
+ *    one GPU (concurrent streams, or host threads) race and must not be
+ *    issued; calls queued one after another on a stream are safe. */
+#define PDA_NOALLOC_MAX_WORKSPACE (64 * 1024 * 1024)
+int paged_decode_attn_noalloc(const pda_shape_t* shape,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              float scale, void* out, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* pda_status_string(int status);
 

@@ -99,6 +99,8 @@ def load_library():
     lib.paged_decode_attn_trace.restype = ctypes.c_int
     lib.paged_decode_attn_workspace_init.argtypes = [P, ctypes.c_int64, P]
     lib.paged_decode_attn_workspace_init.restype = ctypes.c_int
+    lib.paged_decode_attn_noalloc.argtypes = [sp, P, P, P, P, P, ctypes.c_float, P, P]
+    lib.paged_decode_attn_noalloc.restype = ctypes.c_int
     lib.pda_status_string.argtypes = [ctypes.c_int]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_build_id.argtypes = []
@@ -273,6 +275,30 @@ def paged_decode_attn_with_plan(q, k_cache, v_cache, block_table, seq_lens, scal
                              workspace=workspace, max_seq_len=max_seq_len, plan=plan,
                              stream=stream, sliding_window=sliding_window, k_scale=k_scale,
                              v_scale=v_scale)
+
+
+PDA_NOALLOC_MAX_WORKSPACE = 64 * 1024 * 1024
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, block_table, seq_lens, scale: float, out,
+                              max_seq_len: Optional[int] = None, stream=None,
+                              sliding_window: int = 0, k_scale: float = 1.0,
+                              v_scale: float = 1.0):
+    """paged_decode_attn into a caller's `out` with the library's static
+    per-GPU workspace: allocates nothing (no torch allocation either).
+    Raises PdaError (PDA_ERR_WORKSPACE) when the device plan's workspace
+    exceeds PDA_NOALLOC_MAX_WORKSPACE.  Calls overlapping on one GPU race."""
+    _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out)
+    if max_seq_len is None:
+        max_seq_len = block_table.shape[1] * k_cache.shape[2]
+    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window, k_scale,
+                               v_scale)
+    rc = load_library().paged_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), float(scale), _ptr(out), _stream(stream))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_noalloc")
+    return out
 
 
 def paged_decode_attn_workspace_init(workspace, stream=None):

@@ -44,6 +44,7 @@ def _units(csrc=CSRC):
     units.append((os.path.join(csrc, "pda_trace.hip"), "trace.o", []))
     units.append((os.path.join(csrc, "pda_probe.hip"), "probe.o", []))
     units.append((os.path.join(csrc, "pda_fill.hip"), "fill.o", []))
+    units.append((os.path.join(csrc, "pda_noalloc.hip"), "noalloc.o", []))
     flags = " ".join(CFLAGS[:1] + [f"--offload-arch={ARCH}", "-packed-fp32-ops",
                                    "-amdgpu-mfma-vgpr-form"])
     units.append((os.path.join(csrc, "pda_host.cpp"), "host.o",
