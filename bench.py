@@ -58,6 +58,27 @@ WORKLOADS = {
                            desc="gemma-like sliding layer, batch 8, 32 query / 16 KV heads, "
                                 "head 128, block 16, 32768-token contexts, 1024-token window, "
                                 "bf16 KV ~N(0,1)"),
+    "sliding-B1-32K": dict(make=lambda: _cfg().cfg3_sliding(1, 32768, device="cuda"),
+                           desc="gemma-like sliding layer, batch 1, 32 query / 16 KV heads, "
+                                "head 128, block 16, 32768-token context, 1024-token window, "
+                                "bf16 KV ~N(0,1)"),
+    "headline-1K": dict(make=lambda: _cfg().cfg2(32, 1024, device="cuda"),
+                        desc="paged GQA decode, batch 1, 32 query / 8 KV heads, head 128, "
+                             "block 16, 1024-token context, bf16 KV ~N(0,1)"),
+    "fp8-headline": dict(make=lambda: _cfg().cfg2(32, 32768, device="cuda", kv_dtype="fp8"),
+                         desc="paged GQA decode, batch 1, 32 query / 8 KV heads, head 128, "
+                              "block 16, 32768-token context, fp8 E4M3 KV with per-tensor "
+                              "scales, bf16 q"),
+    "fp8-cfg4-32K": dict(make=lambda: _cfg().cfg4(32768, device="cuda", kv_dtype="fp8"),
+                         desc="low-parallelism decode, batch 1, 24 query / 4 KV heads, head "
+                              "256, block 784, 32768-token context, fp8 E4M3 KV, bf16 q"),
+    "tp2-share-12-2-32K": dict(make=lambda: _cfg().cfg4_tp2(32768, device="cuda"),
+                               desc="one GPU's share of the low-parallelism layer under two-way "
+                                    "tensor parallelism: batch 1, 12 query / 2 KV heads, head "
+                                    "256, block 784, 32768-token context, bf16 KV"),
+    "q4-headline": dict(make=lambda: _cfg().cfg2(32, 32768, device="cuda", q_len=4),
+                        desc="four-row decode, batch 1, 32 query / 8 KV heads, head 128, "
+                             "block 16, 32768-token context, bf16 KV"),
 }
 
 
@@ -188,6 +209,34 @@ def summary(name, case, r):
             "passes_us": [round(p["call_ms"] * 1e3, 3) for p in r["passes"]]}
 
 
+def score(case, out, ref=None):
+    """The row's parity ledger entry: rel-L-inf of the GPU output against the
+    oracle over the whole call (the pages' metric: against the oracle's own
+    output scale), the worst per-sequence figure, and the count of
+    non-finite output elements.  `ref` is the oracle's output if already
+    computed."""
+    import numpy as np
+    import oracle
+    import kvgen
+    g = out.float().cpu().numpy()
+    if ref is None:
+        q, k, v, lens = kvgen.oracle_inputs(case)
+        sc = (case.k_scale, case.v_scale) if case.kv_dtype == "fp8" else None
+        if case.q_len > 1:
+            ref = oracle.decode_multi(q, k, v, lens, case.scale, window=case.sliding_window,
+                                      kv_scales=sc)
+        else:
+            ref = oracle.decode(q, k, v, lens, case.scale, window=case.sliding_window,
+                                kv_scales=sc)
+    nan = int(np.count_nonzero(~np.isfinite(g)))
+    per_seq = [oracle.rel_linf(g[b], ref[b]) for b in range(case.B)]
+    tol = {"bf16": 1e-2, "fp16": 2e-3}[case.dtype]
+    return {"rel_linf": float(f"{oracle.rel_linf(g, ref):.4e}"),
+            "rel_linf_worst_seq": float(f"{max(per_seq):.4e}"),
+            "nonfinite": nan, "tol": tol,
+            "pass": bool(nan == 0 and max(per_seq) <= tol and oracle.rel_linf(g, ref) <= tol)}
+
+
 def kernel_source_hash(variant: str = "mfma") -> str:
     """sha256 over the sources the split-KV kernel of `variant` is compiled
     from (its translation unit, the device and common headers, the C ABI
@@ -252,6 +301,31 @@ def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 20
                     "non-temporal loads (pda_read_probe), best grid size"}
 
 
+def cpu_identity() -> dict:
+    """The host CPU as /proc/cpuinfo and the scheduler report it: model name,
+    family / model / stepping, clock, logical CPUs visible and usable."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" not in ln:
+                    if info:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (x.strip() for x in ln.split(":", 1))
+                if k in ("vendor_id", "model name", "cpu family", "model", "stepping",
+                         "cpu MHz", "cache size") and k not in info:
+                    info[k] = v
+    except OSError:
+        pass
+    info["logical_cpus"] = os.cpu_count()
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return info
+
+
 def cpu_baseline(case, seconds):
     """The oracle as it stands, on the host cores, over the same workload."""
     import oracle
@@ -274,23 +348,44 @@ def cpu_baseline(case, seconds):
         oracle.decode(q, k, v, lens, case.scale, nthreads=1, window=case.sliding_window)
         t1 += time.perf_counter() - t0
         n1 += 1
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
-                         model)
-    except OSError:
-        pass
+    model = cpu_identity()
     return ref, {"value": round(case.kv_bytes() / per_call / 1e9, 3), "unit": "GB/s",
                  "cores": threads, "kind": "oracle",
                  "us_per_call": round(per_call * 1e6, 1),
                  "sample": f"{n} full decode call(s) of the headline workload "
                            f"({case.B}x{case.Hq} rows over {sum(case.seq_lens)} tokens), "
-                           f"{t:.1f} s of CPU time, OpenMP over rows",
+                           f"{t:.1f} s of wall-clock time (time.perf_counter around each "
+                           f"call), OpenMP over rows on {threads} threads",
+                 "timer": "wall-clock",
                  "single_thread": {"value": round(case.kv_bytes() / (t1 / n1) / 1e9, 3),
                                    "unit": "GB/s", "us_per_call": round(t1 / n1 * 1e6, 1),
-                                   "sample": f"{n1} call(s), {t1:.1f} s"},
+                                   "sample": f"{n1} call(s), {t1:.1f} s of wall-clock time"},
                  "cpu_model": model}
+
+
+def render_table(line: dict) -> str:
+    """Markdown table of a bench JSON line: the headline row, then every
+    extra row, each with its plan, call and kernel time and fraction of the
+    8 TB/s peak, and its parity entry (rel-L-inf, worst sequence, non-finite
+    count)."""
+    rows = [line["headline"]] + [v for v in line.get("extra", {}).values() if isinstance(v, dict)]
+    if line.get("parity") is not None:
+        rows[0] = dict(rows[0], parity=line["parity"])
+    out = ["| workload | variant | merge | P x T_p | us/call | % of 8 TB/s | split-KV kernel us "
+           "(% peak) | rel-Linf (worst seq) | non-finite |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        par = r.get("parity")
+        ptxt = "-" if par is None else f"{par['rel_linf']:.2e} ({par['rel_linf_worst_seq']:.2e})"
+        ntxt = "-" if par is None else str(par["nonfinite"])
+        out.append(f"| {r['workload']} | {r['variant']} | {r['merge']} | {r['P']} x {r['T_p']} | "
+                   f"{r['us_per_call']:.2f} | {r['pct_of_peak']:.1f} % | "
+                   f"{r['splitkv_kernel_us']:.2f} ({r['kernel_pct_of_peak']:.1f} %) | {ptxt} | "
+                   f"{ntxt} |")
+    slopes = {k: v for k, v in line.get("extra", {}).items() if not isinstance(v, dict)}
+    for k, v in slopes.items():
+        out.append(f"\n{k}: {v}")
+    return "\n".join(out)
 
 
 def main():
@@ -303,9 +398,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle comparison of the extra rows")
+    ap.add_argument("--table", metavar="JSON",
+                    help="print the markdown table of a stored bench line and exit")
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS),
                     help="the timed workload (default: the headline one)")
     args = ap.parse_args()
+    if args.table:
+        with open(args.table) as f:
+            print(render_table(json.loads(f.readline())))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -334,7 +437,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         ref, cpu = cpu_baseline(case, args.cpu_seconds)
-        parity = oracle.rel_linf(r["out"].float().cpu().numpy(), ref)
+        parity = score(case, r["out"], ref)
 
     extra = {}
     if not args.no_extra:
@@ -366,6 +469,8 @@ def main():
             c = mk()
             rr = time_case(c, small_steps, max(5, args.warmup // 4), passes=3)
             extra[name] = summary(name, c, rr)
+            if not args.no_parity:
+                extra[name]["parity"] = score(c, rr["out"])
             del c, rr
             torch.cuda.empty_cache()
         # decode time added per token of context: the slope of us/call over each ladder
@@ -413,10 +518,14 @@ def main():
                      "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": measured_traffic(head["variant"]),
                      "kernel_us": round(r["kernel_ms"] * 1e3, 3),
+                     "call_frac": round(head["GBps"] / PEAK_GBS, 4),
+                     "call_us": head["us_per_call"],
                      "algorithmic_bytes_per_launch": kbytes},
         "cpu_baseline": cpu,
         "read_probe": probe,
-        "parity_rel_linf_vs_oracle": parity,
+        "parity_rel_linf_vs_oracle": None if parity is None else parity["rel_linf"],
+        "parity": parity,
+        "headline": head,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)

@@ -69,8 +69,11 @@
  * undefined behaviour):
  *  - 0 <= seq_lens[b] <= max_seq_len <= max_blocks_per_seq * block_size;
  *  - block_table[b][j] is in [0, num_blocks) for j < ceil(seq_lens[b] / block_size);
- *    entries at or past that index are never read (with a sliding window,
- *    neither are entries of blocks that end before the window);
+ *    the whole row [b][0, max_blocks_per_seq) must be readable memory: the
+ *    kernels may load entries at or past that index (the first tiles'
+ *    entries are loaded before the length is known, and prefetches past a
+ *    partition's end load clamped entries), but such an entry never
+ *    addresses K or V, and block ids are clamped into [0, num_blocks);
  *  - K/V slots at or past seq_lens[b] may hold anything (NaN, Inf, garbage);
  *  - seq_lens[b] == 0 yields a zero output row.
  */

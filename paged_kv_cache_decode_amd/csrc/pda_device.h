@@ -347,6 +347,44 @@ __device__ inline TileBlock tile_block(const DecodeParams& p, const int32_t* row
     return tile_block_of(p, table_entry(row, lb), lb, tile_base);
 }
 
+// A wave's first two tiles on the aligned path: tile `wave` and tile
+// `wave + kWaves` of partition `part` (tt tokens each).  The decode kernels
+// load their table entries together with seq_lens, before the context length
+// is known, at the positions the tiles have when the partition grid starts at
+// token 0 (first_tile_entries).  Once the length is known, first_tile_blocks
+// keeps those entries unless a sliding window moved the grid (base != 0) or,
+// without buffer loads, a tile lies past the end (such a prefetch re-reads
+// the last tile); otherwise it looks the blocks up again.  The trace kernel
+// takes the same two steps, so the bit-exact trace covers the early loads.
+struct FirstTiles {
+    int lb[2];  // logical block indices (clamped into the row)
+    int e[2];   // their table entries
+};
+__device__ inline FirstTiles first_tile_entries(const DecodeParams& p, const int32_t* row,
+                                                int part, int wave, int tt) {
+    FirstTiles f;
+    const int ts = part * p.tokens_per_part + wave * tt;
+    f.lb[0] = tile_table_index(p, ts);
+    f.lb[1] = tile_table_index(p, ts + kWaves * tt);
+    f.e[0] = table_entry(row, f.lb[0]);
+    f.e[1] = table_entry(row, f.lb[1]);
+    return f;
+}
+__device__ inline void first_tile_blocks(const DecodeParams& p, const int32_t* row,
+                                         const FirstTiles& f, int part, int wave, int tt,
+                                         const SeqRange& rg, int t0, int ntiles, bool buf,
+                                         TileBlock (&first)[2]) {
+    const int ts = part * p.tokens_per_part + wave * tt;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int jj = wave + st * kWaves;
+        if (rg.base != 0 || (!buf && jj >= ntiles))
+            first[st] = tile_block(p, row, t0 + (buf ? jj : min(jj, ntiles - 1)) * tt);
+        else
+            first[st] = tile_block_of(p, f.e[st], f.lb[st], ts + st * kWaves * tt);
+    }
+}
+
 // In-tile offset of the row a lane reads for in-tile offset o: tokens at or
 // past t1 (the partition end, never past the sequence end) are redirected to
 // token t1-1, and tokens before lo (the first token attended to) to lo, so no
@@ -523,6 +561,67 @@ __device__ inline float4 load_coherent16(const float* base, uint32_t off) {
                        __uint_as_float(v.w));
 }
 
+// 8 bytes of the workspace at base + off (8-byte aligned), read like
+// load_coherent16.
+__device__ inline float2 load_coherent8(const float* base, uint32_t off) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(uniform_rsrc(base), off, 0, kBufferSc1);
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
+
+#ifndef PDA_FUSED_ONE_TRIP
+#define PDA_FUSED_ONE_TRIP 1
+#endif
+// The fused merge in one memory round trip (up to kMergeUnroll partitions):
+// each thread takes four consecutive elements of one row and issues the
+// loads of every partition's (m, l) pair and of its four partial elements
+// together, then forms the weights itself (every thread of a row the same
+// ones): M = max over p, w_p = l_p 2^(m_p - M), the sums over p in index
+// order, times 1 / sum w_p -- the rule of merge_unit below, with no LDS
+// step and no barrier between the two kinds of loads.
+template <typename Elt, int D>
+__device__ inline void merge_unit_one_trip(const DecodeParams& p, int b, int g, int Pb) {
+    constexpr int D4 = D / 4;
+    constexpr int U = kMergeUnroll;
+    uint16_t* out16 = static_cast<uint16_t*>(p.out);
+    const int R = p.rows, P = p.num_partitions;
+    const int64_t row0 = row_index(p, b, g, 0);
+    const float* obase = p.ws_o + row0 * P * D;
+    const float* mbase = p.ws_ml + row0 * P * 2;
+    for (int it = threadIdx.x; it < R * D4; it += blockDim.x) {
+        const int i = it / D4, c = it - i * D4;
+        const int64_t rrel = row_index(p, b, g, i) - row0;
+        const uint32_t ooff = (uint32_t)((rrel * P * D + 4 * c) * sizeof(float));
+        const uint32_t moff = (uint32_t)(rrel * P * 2 * sizeof(float));
+        float2 ml[U];
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = min(u, Pb - 1);  // past Pb: re-read the last, never used
+            ml[u] = load_coherent8(mbase, moff + (uint32_t)(q * 2 * sizeof(float)));
+            v[u] = load_coherent16(obase, ooff + (uint32_t)(q * D * sizeof(float)));
+        }
+        float M = -FLT_MAX;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < Pb) M = fmaxf(M, ml[u].x);
+        float den = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float w = u < Pb ? ml[u].y * fast_exp2(ml[u].x - M) : 0.f;
+            if (u < Pb) den += w;
+            acc.x += w * v[u].x; acc.y += w * v[u].y;
+            acc.z += w * v[u].z; acc.w += w * v[u].w;
+        }
+        const float f = den > 0.f ? 1.f / den : 0.f;
+        uint16_t* dst = out16 + (row0 + rrel) * D + 4 * c;
+        dst[0] = Elt::from_float(acc.x * f);
+        dst[1] = Elt::from_float(acc.y * f);
+        dst[2] = Elt::from_float(acc.z * f);
+        dst[3] = Elt::from_float(acc.w * f);
+    }
+}
+
 template <typename Elt, int D>
 __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
     __shared__ float s_w[kMergePairs];
@@ -624,6 +723,9 @@ __device__ void merge_unit(const DecodeParams& p, int b, int g, int Pb) {
 // counts the arrival with a device-scope atomic.  The last arrival resets the
 // counter for the next call and reads the partials back with device-scope
 // loads.  No L2 write-back or invalidate is needed.
+#ifndef PDA_FUSED_ACQREL
+#define PDA_FUSED_ACQREL 0
+#endif
 template <typename Elt, int D>
 __device__ inline void fused_merge_tail(const DecodeParams& p, const SeqRange& rg, int b,
                                         int g) {
@@ -633,12 +735,25 @@ __device__ inline void fused_merge_tail(const DecodeParams& p, const SeqRange& r
     const int Pb = live_partitions(p, rg);
     if (threadIdx.x == 0) {
         int32_t* ctr = p.counters + (int64_t)b * p.num_kv_heads + g;
+#if PDA_FUSED_ACQREL
+        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+#else
         const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
         s_last = old == Pb - 1;
         if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
-    if (s_last) merge_unit<Elt, D>(p, b, g, Pb);
+    if (!s_last) return;
+#if PDA_FUSED_ONE_TRIP
+    const int64_t span = (row_index(p, b, g, p.rows - 1) - row_index(p, b, g, 0) + 1) *
+                         p.num_partitions * D * 4;
+    if (Pb <= kMergeUnroll && span < ((int64_t)1 << 31)) {
+        merge_unit_one_trip<Elt, D>(p, b, g, Pb);
+        return;
+    }
+#endif
+    merge_unit<Elt, D>(p, b, g, Pb);
 }
 
 // Zero output rows of the R rows of (b, g) (an empty context).

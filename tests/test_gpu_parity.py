@@ -216,6 +216,32 @@ def test_fused_and_kernel_merge_reuse_workspace(mk):
     assert int(ctr.abs().sum().item()) == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fused_merge_across_xcds_repeated(dtype):
+    """One KV head at batch 1 under a forced 16-partition fused plan: the
+    dispatcher sends workgroup L of the (Hkv, B, P) grid to XCD L mod 8, so
+    the 16 partitions of the unit run on all eight XCDs and the last one to
+    arrive reads partials written on the seven others.  40 calls in a row on
+    one workspace: every output bit-identical to the first and within
+    tolerance of the oracle, the arrival counter back at zero."""
+    case = to_device(kvgen.make_case(1, 8, 1, 128, 16, [16000], dtype=dtype, seed=404,
+                                     tail_k="nan", tail_v="nan"))
+    plan = plan_of(16, 1024, variant=pda.PDA_VARIANT_MFMA, merge=pda.PDA_MERGE_FUSED)
+    shape = shape_of(case)
+    ws = torch.zeros(pda.pda_workspace_bytes(shape, plan), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(40):
+        outs.append(pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                          case.seq_lens_t, case.scale, workspace=ws,
+                                          max_seq_len=case.max_seq_len, plan=plan))
+    torch.cuda.synchronize()
+    check(case, outs[0])
+    first = bits(outs[0])
+    for o in outs[1:]:
+        assert np.array_equal(first, bits(o))
+    assert int(ws[:16384 * 4].view(torch.int32).abs().sum().item()) == 0
+
+
 def test_one_workspace_serves_a_sequence_of_shapes():
     """Zeroed once, one workspace serves calls of different shapes under the
     device plan, fused merge and merge kernel alike: the arrival counters sit
