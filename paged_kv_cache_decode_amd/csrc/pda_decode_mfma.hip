@@ -161,14 +161,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
     }
     const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
-    TileBlock first[2] = {{0, 0}, {0, 0}};
+    FirstTiles ft{{0, 0}, {0, 0}};
     if constexpr (ALIGNED) {
-        const int ts = part * p.tokens_per_part + wave * TT;
-        const int lb0 = tile_table_index(p, ts), lb1 = tile_table_index(p, ts + kWaves * TT);
-        const int e0 = table_entry(trow, lb0), e1 = table_entry(trow, lb1);
-        keep_issued(raw_len, e0, e1);
-        first[0] = tile_block_of(p, e0, lb0, ts);
-        first[1] = tile_block_of(p, e1, lb1, ts + kWaves * TT);
+        ft = first_tile_entries(p, trow, part, wave, TT);
+        keep_issued(raw_len, ft.e[0], ft.e[1]);
     }
     issue_fence();
 
@@ -206,14 +202,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(ALIGNED || !BUF, "buffer loads need the aligned path");
     constexpr bool kBuf = BUF;
     auto tile_start = [&](int jj) { return t0 + (kBuf ? jj : min(jj, ntiles - 1)) * TT; };
-    if constexpr (ALIGNED) {
-        // the speculative entries hold for the tiles the wave will load
-        // unless a sliding window moved the partition, or (without buffer
-        // loads) the second tile is past the end and re-reads the last one
-        if (rg.base != 0) first[0] = tile_block(p, trow, tile_start(wave));
-        if (rg.base != 0 || (!kBuf && wave + kWaves >= ntiles))
-            first[1] = tile_block(p, trow, tile_start(wave + kWaves));
-    }
+    TileBlock first[2] = {{0, 0}, {0, 0}};
+    if constexpr (ALIGNED)
+        first_tile_blocks(p, trow, ft, part, wave, TT, rg, t0, ntiles, kBuf, first);
     // `tb` is the tile's block on the aligned path (tile_block of tile_start)
     auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[KL], VRaw (&vr)[4][DH]) {
         const bool valid = jj < ntiles;

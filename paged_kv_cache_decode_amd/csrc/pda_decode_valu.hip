@@ -78,14 +78,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     }
     const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
     static_assert(S == 3, "the first-tile table entries are kept for S - 1 = 2 tiles");
-    TileBlock first[S - 1] = {{0, 0}, {0, 0}};
+    FirstTiles ft{{0, 0}, {0, 0}};
     if constexpr (ALIGNED) {
-        const int ts = part * p.tokens_per_part + wave * TT;
-        const int lb0 = tile_table_index(p, ts), lb1 = tile_table_index(p, ts + kWaves * TT);
-        const int e0 = table_entry(trow, lb0), e1 = table_entry(trow, lb1);
-        keep_issued(raw_len, e0, e1);
-        first[0] = tile_block_of(p, e0, lb0, ts);
-        first[1] = tile_block_of(p, e1, lb1, ts + kWaves * TT);
+        ft = first_tile_entries(p, trow, part, wave, TT);
+        keep_issued(raw_len, ft.e[0], ft.e[1]);
     }
     issue_fence();
 
@@ -126,15 +122,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // schedule of the buffer form loses ~1%).
     constexpr bool kBuf = ALIGNED && GP == 1;
     auto tile_start = [&](int jj) { return t0 + (kBuf ? jj : min(jj, ntiles - 1)) * TT; };
-    if constexpr (ALIGNED) {
-        // the speculative entries hold for the tiles the wave will load
-        // unless a sliding window moved the partition, or (without buffer
-        // loads) a tile is past the end and re-reads the last one
-#pragma unroll
-        for (int st = 0; st < S - 1; ++st)
-            if (rg.base != 0 || (!kBuf && wave + st * kWaves >= ntiles))
-                first[st] = tile_block(p, trow, tile_start(wave + st * kWaves));
-    }
+    TileBlock first[S - 1] = {{0, 0}, {0, 0}};
+    if constexpr (ALIGNED)
+        first_tile_blocks(p, trow, ft, part, wave, TT, rg, t0, ntiles, kBuf, first);
     // `tb` is the tile's block on the aligned path (tile_block of tile_start)
     auto load_tile = [&](int jj, const TileBlock& tb, uint4 (&kr)[U], uint4 (&vr)[U]) {
         const bool valid = jj < ntiles;

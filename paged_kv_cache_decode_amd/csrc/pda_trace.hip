@@ -2,10 +2,13 @@
 //
 // Same grid, partition bounds, table staging, tile walk and row location
 // (stage_table_slice, locate_token / locate_row and the lane-to-row maps of
-// ValuGeom and MfmaGeom) as the decode kernels, but each lane that would load
-// a token row records which physical slot and which partition it used,
-// instead of loading it.  ROWS selects whose rows: 0 the VALU kernel's (K and
-// V alike), 1 the MFMA kernel's K rows, 2 its V rows.  Tests compare the
+// ValuGeom and MfmaGeom) as the decode kernels -- on the aligned path also
+// the blocks of each wave's first two tiles from the table entries loaded
+// before the context length is known (first_tile_entries /
+// first_tile_blocks) -- but each lane that would load a token row records
+// which physical slot and which partition it used, instead of loading it.
+// ROWS selects whose rows: 0 the VALU kernel's (K and V alike), 1 the MFMA
+// kernel's K rows, 2 its V rows.  Tests compare the
 // trace bit for bit with a recomputation from the definition of the paged
 // cache.
 #include "pda_device.h"
@@ -23,6 +26,9 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int c = lane % LPT, r = lane / LPT;
+    const int32_t* trow = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+    FirstTiles ft{{0, 0}, {0, 0}};
+    if constexpr (ALIGNED) ft = first_tile_entries(p, trow, part, wave, TT);
     const SeqRange rg = seq_range(p, b);
     const int L = rg.L;
     const int t0 = rg.base + part * p.tokens_per_part;
@@ -42,6 +48,24 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     const int32_t* tv = table_view<ALIGNED>(p, b, tbl);
     const int tlb0 = ALIGNED ? 0 : lb0;
     const int ntiles = (t1 - t0 + TT - 1) / TT;
+    // the decode kernels' buffer-load choice on the aligned path: always for
+    // the matrix-core kernel, for one packed row in the VALU kernel
+    const bool buf = ALIGNED && (ROWS != 0 || p.rows == 1);
+    TileBlock first[2] = {{0, 0}, {0, 0}};
+    if constexpr (ALIGNED)
+        first_tile_blocks(p, trow, ft, part, wave, TT, rg, t0, ntiles, buf, first);
+    // the row a lane would load at in-tile offset o of tile j: the first two
+    // tiles of the wave from the early entries, the rest looked up
+    auto locate = [&](int j, int tile_base, int o, int& phys, int& slot0, int& dt) {
+        if (ALIGNED && (j == wave || j == wave + kWaves)) {
+            const TileBlock& tb = first[j == wave ? 0 : 1];
+            phys = tb.phys;
+            slot0 = tb.slot0;
+            dt = tile_row(tile_base, rg.lo, t1, o);
+        } else {
+            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, o, phys, slot0, dt);
+        }
+    };
     auto record = [&](int t, int phys, int slot) {
         const int64_t at = unit * p.max_seq_len + t;
         p.trace_slot[at] = phys * p.block_size + slot;
@@ -53,21 +77,20 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
         if constexpr (ROWS == 0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                locate_token<R, ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, u, r, phys, slot0,
-                                         dt);
+                locate(j, tile_base, u * R + r, phys, slot0, dt);
                 const int t = tile_base + u * R + r;
                 if (c == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
         } else if constexpr (ROWS == 1) {
             const int o = mfma_k_offset(lane);
-            locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, o, phys, slot0, dt);
+            locate(j, tile_base, o, phys, slot0, dt);
             const int t = tile_base + o;
             if ((lane >> 4) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int o = mfma_v_offset(lane, rr);
-                locate_row<ALIGNED>(p, tv, tlb0, tile_base, rg.lo, t1, o, phys, slot0, dt);
+                locate(j, tile_base, o, phys, slot0, dt);
                 const int t = tile_base + o;
                 if ((lane & 15) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
