@@ -127,7 +127,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(S >= 2 && S <= 6, "stages");
     constexpr int KL = F8 ? KS / 2 : KS;       // 16-byte K loads per lane and tile
     using VRaw = typename std::conditional<F8, uint2, uint4>::type;  // 8 V elements
-    extern __shared__ float smem[];
+    // 16-byte aligned: the static LDS of the merge tail (4228 bytes) comes
+    // first, and a 4-byte aligned base made every 8- and 16-byte access of
+    // the epilogue a misaligned one
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     float* red = smem;                                                       // [kWaves][8][D+2]
     constexpr int HC = mfma_row_chunk(D);  // rows staged in LDS at a time
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * HC * (D + 2));
@@ -340,6 +343,25 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
 #pragma unroll
         for (int dh = 0; dh < DH; ++dh) {
+            if constexpr (F8) {
+                // byte e of the four rounds (tokens 4*q4 + r, in order) into
+                // one word, which two packed conversions turn into the A
+                // operand of element e
+                uint32_t tb[8];
+                byte_transpose4(vr[0][dh].x, vr[1][dh].x, vr[2][dh].x, vr[3][dh].x,
+                                *reinterpret_cast<uint32_t(*)[4]>(&tb[0]));
+                byte_transpose4(vr[0][dh].y, vr[1][dh].y, vr[2][dh].y, vr[3][dh].y,
+                                *reinterpret_cast<uint32_t(*)[4]>(&tb[4]));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint2 a = make_uint2(fp8x2_to_16bit<Elt, false>(tb[e]),
+                                               fp8x2_to_16bit<Elt, true>(tb[e]));
+#pragma unroll
+                    for (int c = 0; c < RC; ++c)
+                        oacc[c][dh][e] = MfmaPV<Elt>::run(a, pb[c], oacc[c][dh][e]);
+                }
+                continue;
+            }
             // the lane's four V rounds (tokens 4*q4 + r) as 16-bit elements
             uint4 w[4];
 #pragma unroll

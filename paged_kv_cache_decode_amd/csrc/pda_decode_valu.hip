@@ -49,7 +49,10 @@ template <typename Elt, int D, int GP, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     using Geo = ValuGeom<D>;
     constexpr int LPT = Geo::LPT, RT = Geo::R, U = Geo::U, TT = Geo::TT;
-    extern __shared__ float smem[];
+    // 16-byte aligned: the static LDS of the merge tail (4228 bytes) comes
+    // first, and a 4-byte aligned base made every 8- and 16-byte access of
+    // the epilogue a misaligned one
+    extern __shared__ __attribute__((aligned(16))) float smem[];
     float* red = smem;                                                  // [kWaves][GP][D+2]
     int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
 

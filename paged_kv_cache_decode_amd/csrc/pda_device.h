@@ -25,10 +25,6 @@ struct BF16 {
     __device__ static inline uint16_t from_float(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
     }
-    // two fp32 values that are bf16 values (low 16 bits zero) packed exactly
-    __device__ static inline uint32_t pack_exact(float lo, float hi) {
-        return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-    }
 };
 
 struct FP16 {
@@ -45,25 +41,53 @@ struct FP16 {
     __device__ static inline uint16_t from_float(float x) {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));  // round to nearest even
     }
-    // two fp32 values that are fp16 values packed exactly (no rounding occurs)
-    __device__ static inline uint32_t pack_exact(float lo, float hi) {
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-    }
 };
 
 // ---- fp8 E4M3 (OCP) KV bytes -------------------------------------------
-// The hardware conversion decodes the OCP E4M3 format exactly (every E4M3
-// value, subnormals and NaN included, is an fp32 value, and also a bf16 and
-// an fp16 value), two bytes of a 32-bit word at a time.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ inline f32x2_t fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, false); }
-__device__ inline f32x2_t fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, true); }
+// Two E4M3 bytes of w (bytes 0 and 1, or 2 and 3 with HI) -> two elements of
+// the 16-bit type in one instruction (v_cvt_scalef32_pk_{bf16,f16}_fp8 with
+// scale 1), low byte to the low half.  The conversion is exact: every E4M3
+// value, subnormals included, is a bf16 and an fp16 value (checked against
+// the conversion through fp32 on all 256 codes).
+template <typename Elt, bool HI>
+__device__ inline uint32_t fp8x2_to_16bit(uint32_t w);
+template <>
+__device__ inline uint32_t fp8x2_to_16bit<BF16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ inline uint32_t fp8x2_to_16bit<BF16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+template <>
+__device__ inline uint32_t fp8x2_to_16bit<FP16, false>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <>
+__device__ inline uint32_t fp8x2_to_16bit<FP16, true>(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+}
+
 // 8 E4M3 bytes -> 8 elements of the 16-bit type, exactly
 template <typename Elt>
 __device__ inline uint4 fp8x8_to_16bit(uint32_t w0, uint32_t w1) {
-    const f32x2_t a = fp8x2_lo(w0), b = fp8x2_hi(w0), c = fp8x2_lo(w1), d = fp8x2_hi(w1);
-    return make_uint4(Elt::pack_exact(a[0], a[1]), Elt::pack_exact(b[0], b[1]),
-                      Elt::pack_exact(c[0], c[1]), Elt::pack_exact(d[0], d[1]));
+    return make_uint4(fp8x2_to_16bit<Elt, false>(w0), fp8x2_to_16bit<Elt, true>(w0),
+                      fp8x2_to_16bit<Elt, false>(w1), fp8x2_to_16bit<Elt, true>(w1));
+}
+
+// Byte transpose of four 32-bit words: out[e] holds byte e of x0, x1, x2, x3
+// in its bytes 0, 1, 2, 3 (v_perm_b32 picks byte k of the 64-bit {hi, lo} for
+// selector value k: 0-3 from lo, 4-7 from hi).
+__device__ inline void byte_transpose4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                       uint32_t (&out)[4]) {
+    const uint32_t a = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+    const uint32_t b = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+    const uint32_t c = __builtin_amdgcn_perm(x3, x2, 0x05010400u);  // x2.b0 x3.b0 x2.b1 x3.b1
+    const uint32_t d = __builtin_amdgcn_perm(x3, x2, 0x07030602u);  // x2.b2 x3.b2 x2.b3 x3.b3
+    out[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);  // a.b0 a.b1 c.b0 c.b1
+    out[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);  // a.b2 a.b3 c.b2 c.b3
+    out[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
 // 2^x with the hardware instruction (v_exp_f32).  Arguments here are
@@ -449,20 +473,31 @@ __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + 
 // staged in LDS as red[w][i][0..D) = unnormalised O, red[w][i][D] = running
 // max m (exp2 domain), red[w][i][D+1] = denominator l (red_heads rows per
 // wave, hn <= min(red_heads, 8)), in a fixed order, and write either the
-// 16-bit output (one partition) or the fp32 partial.  32 threads per row
-// (8 rows at a time): each computes its row's wave weights once and then
-// D/32 consecutive elements, read from LDS in pairs and stored together.
+// 16-bit output (one partition) or the fp32 partial.  32 threads per row (8
+// rows at a time); thread j of a row takes the element pairs d = 2j + 64k
+// (k < D/64), so a row's threads read 64 consecutive floats of LDS per pair
+// (8 consecutive elements per thread put threads 4 apart on the same banks)
+// and write 256 contiguous bytes of output or partials per pair and row.
+// All LDS reads of the step are issued before any arithmetic.
 template <typename Elt, int D>
 __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, int red_heads,
                                        int h0, int hn, int b, int g, int part) {
-    constexpr int kTpr = 32;                 // threads per row
-    constexpr int kDpt = D / kTpr;           // consecutive elements per thread: 2, 4 or 8
-    static_assert(kDpt % 2 == 0 && kThreads == 8 * kTpr, "rows of 32 threads, element pairs");
-    const int i = threadIdx.x / kTpr, d0 = (threadIdx.x % kTpr) * kDpt;
+    constexpr int kTpr = 32;        // threads per row
+    constexpr int KP = D / 64;      // element pairs per thread: 1, 2 or 4
+    static_assert(kThreads == 8 * kTpr, "rows of 32 threads");
+    const int i = threadIdx.x / kTpr, j = threadIdx.x % kTpr;
     if (i >= hn) return;
-    float mw[kWaves];
+    // every LDS read of the step first: the waves' (m, l) and the row's pairs
+    float mw[kWaves], lw[kWaves];
+    float2 vw[kWaves][KP];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mw[w] = red[(w * red_heads + i) * (D + 2) + D];
+    for (int w = 0; w < kWaves; ++w) {
+        const float* rw = red + (w * red_heads + i) * (D + 2);
+        mw[w] = rw[D];
+        lw[w] = rw[D + 1];
+#pragma unroll
+        for (int k = 0; k < KP; ++k) vw[w][k] = *reinterpret_cast<const float2*>(rw + 2 * j + 64 * k);
+    }
     float M = -FLT_MAX;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mw[w]);
@@ -470,71 +505,71 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
         wt[w] = fast_exp2(mw[w] - M);
-        den += red[(w * red_heads + i) * (D + 2) + D + 1] * wt[w];
+        den += lw[w] * wt[w];
     }
     // a row with no token in this partition (a causal row ending before it)
     // has den == 0: its normalised partial is 0, and its weight l = 0 keeps
     // it out of the merge.  v_scale (1 for 16-bit KV) dequantises fp8 V; the
     // merge is linear in o, so it applies to partials too.
     const float f = den > 0.f ? p.v_scale / den : 0.f;
-    float o[kDpt];
+    float2 o[KP];
 #pragma unroll
-    for (int e = 0; e < kDpt; ++e) o[e] = 0.f;
+    for (int k = 0; k < KP; ++k) o[k] = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float2* src = reinterpret_cast<const float2*>(red + (w * red_heads + i) * (D + 2) + d0);
+    for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-        for (int e = 0; e < kDpt / 2; ++e) {
-            const float2 v = src[e];
-            o[2 * e] += v.x * wt[w];
-            o[2 * e + 1] += v.y * wt[w];
+        for (int k = 0; k < KP; ++k) {
+            o[k].x += vw[w][k].x * wt[w];
+            o[k].y += vw[w][k].y * wt[w];
         }
-    }
 #pragma unroll
-    for (int e = 0; e < kDpt; ++e) o[e] *= f;
+    for (int k = 0; k < KP; ++k) {
+        o[k].x *= f;
+        o[k].y *= f;
+    }
     const int64_t row = row_index(p, b, g, h0 + i);
     if (p.num_partitions == 1) {
-        uint32_t pk[kDpt / 2];
+        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + row * D);
 #pragma unroll
-        for (int e = 0; e < kDpt / 2; ++e)
-            pk[e] = (uint32_t)Elt::from_float(o[2 * e]) |
-                    ((uint32_t)Elt::from_float(o[2 * e + 1]) << 16);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + row * D + d0);
-#pragma unroll
-        for (int e = 0; e < kDpt / 2; ++e) dst[e] = pk[e];
+        for (int k = 0; k < KP; ++k)
+            dst[j + 32 * k] = (uint32_t)Elt::from_float(o[k].x) |
+                              ((uint32_t)Elt::from_float(o[k].y) << 16);
         return;
     }
     const int64_t prow = row * p.num_partitions + part;
-    float* dst = p.ws_o + prow * D + d0;
     if (p.fused_merge) {  // read back by another workgroup of this launch
-        // offsets from the unit's first row: its partials span R' rows of
-        // P x D floats (R' = R, or more rows apart with q_len > 1)
         const int64_t row0 = row_index(p, b, g, 0);
         const int64_t span = (row_index(p, b, g, p.rows - 1) - row0 + 1) * p.num_partitions * D * 4;
         if (span < ((int64_t)1 << 31)) {
             const int64_t prel = (row - row0) * p.num_partitions + part;
             float* obase = p.ws_o + row0 * p.num_partitions * D;
-            const uint32_t off = (uint32_t)((prel * D + d0) * 4);
+            const uint32_t off = (uint32_t)((prel * D + 2 * j) * 4);
 #pragma unroll
-            for (int e = 0; e < kDpt; e += (kDpt % 4 == 0 ? 4 : 2))
-                store_coherent_vec<kDpt % 4 == 0 ? 4 : 2>(obase, off + 4 * e, o + e);
-            if (d0 == 0) {
+            for (int k = 0; k < KP; ++k) {
+                const float v2[2] = {o[k].x, o[k].y};
+                store_coherent_vec<2>(obase, off + 256 * k, v2);
+            }
+            if (j == 0) {
                 const float mlv[2] = {M, den};
                 store_coherent_vec<2>(p.ws_ml + row0 * p.num_partitions * 2, (uint32_t)(prel * 8), mlv);
             }
         } else {
+            float* dst = p.ws_o + prow * D;
 #pragma unroll
-            for (int e = 0; e < kDpt; ++e) store_coherent(dst + e, o[e]);
-            if (d0 == 0) {
+            for (int k = 0; k < KP; ++k) {
+                store_coherent(dst + 2 * j + 64 * k, o[k].x);
+                store_coherent(dst + 2 * j + 64 * k + 1, o[k].y);
+            }
+            if (j == 0) {
                 store_coherent(p.ws_ml + prow * 2, M);
                 store_coherent(p.ws_ml + prow * 2 + 1, den);
             }
         }
     } else {              // read by the merge kernel after this launch
+        float2* dst = reinterpret_cast<float2*>(p.ws_o + prow * D);
 #pragma unroll
-        for (int e = 0; e < kDpt / 2; ++e)
-            reinterpret_cast<float2*>(dst)[e] = make_float2(o[2 * e], o[2 * e + 1]);
-        if (d0 == 0) reinterpret_cast<float2*>(p.ws_ml)[prow] = make_float2(M, den);
+        for (int k = 0; k < KP; ++k) dst[j + 32 * k] = o[k];
+        if (j == 0) reinterpret_cast<float2*>(p.ws_ml)[prow] = make_float2(M, den);
     }
 }
 

@@ -76,6 +76,69 @@ def test_fp8_parity(D, bs, G, lens, n, W, dtype):
         check(case, run(case, plan=plan), ref, per_seq=True)
 
 
+# every finite E4M3 code (the two NaN codes, 0x7F and 0xFF, read as 0)
+FINITE_CODES = np.array([c if c not in (0x7F, 0xFF) else 0 for c in range(256)], dtype=np.uint8)
+
+
+def _one_block_fp8(B, Hq, D, rows, dtype, q, scale):
+    """B sequences of len(rows) tokens sharing one physical block of 16 slots
+    whose K and V rows are the given (k_bytes, v_bytes) pairs; the tail
+    slots and the second block hold NaN codes."""
+    kc = torch.full((2, 1, 16, D), 0x7F, dtype=torch.uint8)
+    vc = torch.full((2, 1, 16, D), 0x7F, dtype=torch.uint8)
+    for t, (kb, vb) in enumerate(rows):
+        kc[0, 0, t] = torch.from_numpy(kb)
+        vc[0, 0, t] = torch.from_numpy(vb)
+    L = len(rows)
+    table = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    out = pda.paged_decode_attn(q.cuda(), kc.cuda().view(torch.float8_e4m3fn),
+                                vc.cuda().view(torch.float8_e4m3fn), table, lens, scale,
+                                max_seq_len=L, k_scale=1.0, v_scale=1.0)
+    torch.cuda.synchronize()
+    k = [np.stack([kb for kb, _ in rows])[None].repeat(1, 0) for _ in range(B)]
+    v = [np.stack([vb for _, vb in rows])[None].repeat(1, 0) for _ in range(B)]
+    ref = oracle.decode(q.float().numpy(), k, v, [L] * B, scale, kv_scales=(1.0, 1.0))
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fp8_every_code_decodes_exactly(dtype):
+    """The kernel's E4M3 decoding, code by code, against the oracle's decoder
+    (written from the format's definition and pinned to torch on all 256
+    codes).  V: a one-token context returns its V row exactly (the softmax of
+    one score is 1), so with v_scale 1 each output element must be the E4M3
+    value of its V byte, bit for bit -- the 16-bit output holds every E4M3
+    value exactly (as values: the sum 0 + 1 x (-0) is +0 for the code of -0,
+    in the oracle too).  K: two tokens, K row 0 zero and V rows 1 and 0, query
+    row (b, h) one-hot at dimension d = 16 b + h, scale 64: the output is the
+    weight of token 0, 1 / (1 + e^(64 K1[d])), a steep function of that one
+    K code (a subnormal read as zero moves it by 3 % or more)."""
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    D = 256
+    gen = torch.Generator().manual_seed(7)
+    q = torch.randn((1, 2, D), generator=gen).to(tdt)
+    one = np.full(D, 0x38, dtype=np.uint8)      # E4M3 1.0
+    out, ref = _one_block_fp8(1, 2, D, [(one, FINITE_CODES)], dtype, q, 0.1)
+    expect = torch.from_numpy(oracle.e4m3_value(FINITE_CODES).astype(np.float32)).to(tdt)
+    for h in range(2):  # value equality: bit equality but for the sign of zero (0 + 1 x -0 = +0)
+        assert torch.equal(out[0, h].cpu().float(), expect.float())
+    assert np.array_equal(ref[0, 0], expect.float().numpy())
+    # K codes through the scores
+    q = torch.zeros((16, 16, D), dtype=tdt)
+    for b in range(16):
+        for h in range(16):
+            q[b, h, 16 * b + h] = 1.0
+    zero = np.zeros(D, dtype=np.uint8)
+    out, ref = _one_block_fp8(16, 16, D, [(zero, one), (FINITE_CODES, zero)], dtype, q, 64.0)
+    got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    # every row's elements are the same weight; compare the weight per (b, h)
+    w_got, w_ref = got[..., 0], ref[..., 0]
+    err = np.abs(w_got - w_ref)
+    assert np.all(err <= 1e-2 * np.abs(w_ref) + 1e-6), float(err.max())
+
+
 @pytest.mark.parametrize("tail", ["nan", "1e4"])
 def test_fp8_poisoned_tails_bit_identical(tail):
     """NaN (S.1111.111) or the largest finite byte in every unwritten slot
