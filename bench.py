@@ -291,6 +291,29 @@ def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 20
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / calls
         rates[wg] = nbytes / (ms * 1e-3) / 1e9
+    # the same bytes as a decode call, on the decode's grid: reads of 128 MiB
+    # (the 16-bit headline's K+V) and 64 MiB (its fp8 form) by 256 workgroups,
+    # rotating over the buffer's slices so that no read finds its slice in the
+    # MALL; and the launch floor (a 16-byte read by one workgroup)
+    def per_launch_us(size, wgs, n=200):
+        nsl = nbytes // size
+        for i in range(4):
+            pda.pda_read_probe(src[(i % nsl) * size:(i % nsl + 1) * size], sink, wgs)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(n):
+            pda.pda_read_probe(src[(i % nsl) * size:(i % nsl + 1) * size], sink, wgs)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+    same = {}
+    for mib in (128, 64):
+        us = per_launch_us(mib << 20, 256)
+        same[f"{mib}MiB_256wg"] = {"us_per_launch": round(us, 3),
+                                   "GBps": round((mib << 20) / (us * 1e-6) / 1e9, 1)}
+    floor_us = per_launch_us(16, 1, n=1000)
     del src
     torch.cuda.empty_cache()
     best = max(rates, key=rates.get)
@@ -298,7 +321,12 @@ def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 20
             "bytes": nbytes, "workgroups": best,
             "GBps_by_workgroups": {str(k): round(v, 1) for k, v in rates.items()},
             "what": "one streaming read of a 4 GiB buffer with the decode kernels' 16-byte "
-                    "non-temporal loads (pda_read_probe), best grid size"}
+                    "non-temporal loads (pda_read_probe), best grid size",
+            "same_bytes_same_grid": same,
+            "launch_floor_us": round(floor_us, 3),
+            "what_same_bytes": "back-to-back reads of 128 MiB and 64 MiB slices of the buffer "
+                               "(rotating, so none is served by the MALL) by 256 workgroups, "
+                               "per launch; launch floor: a 16-byte read by one workgroup"}
 
 
 def cpu_identity() -> dict:

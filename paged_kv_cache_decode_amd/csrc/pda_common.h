@@ -124,6 +124,13 @@ int run_decode(const pda_shape_t* s, const pda_plan_t* pl, const void* q, const 
                float scale, void* out, void* workspace, int64_t workspace_bytes, void* stream,
                hipEvent_t ev0, hipEvent_t ev1);
 
+// Floats per staged row of the unit epilogue in LDS: D values, the running
+// max m and the denominator l, and two floats of padding, so that rows start
+// 16 bytes apart (with the 16-byte aligned LDS base, every 8- and 16-byte
+// access is aligned) and the matrix-core layout's 16-byte row writes of up to
+// 8 rows fall on distinct banks (D + 2 put two rows' writes on each bank).
+__host__ __device__ constexpr int lds_row_floats(int head_size) { return head_size + 4; }
+
 // Rows the MFMA kernel stages in LDS at once at the end of a unit: 16 (a
 // whole 16-row matrix-core chunk, one barrier) up to head size 128, 8 at 256
 // (LDS).
@@ -133,7 +140,7 @@ __host__ __device__ constexpr int mfma_row_chunk(int head_size) {
 
 // Bytes of dynamic LDS the MFMA kernel uses (rows staged mfma_row_chunk at a time).
 inline size_t mfma_lds_bytes(int head_size, int tbl_capacity) {
-    return (size_t)kWaves * mfma_row_chunk(head_size) * (head_size + 2) * sizeof(float) +
+    return (size_t)kWaves * mfma_row_chunk(head_size) * lds_row_floats(head_size) * sizeof(float) +
            (size_t)tbl_capacity * sizeof(int32_t);
 }
 
@@ -149,7 +156,7 @@ inline int valu_group_pad(int g) {
 // Bytes of dynamic LDS the decode kernel uses for a block-table slice of
 // `tbl_capacity` entries plus the cross-wave merge of `gpad` heads.
 inline size_t decode_lds_bytes(int head_size, int gpad, int tbl_capacity) {
-    size_t merge = (size_t)kWaves * gpad * (head_size + 2) * sizeof(float);
+    size_t merge = (size_t)kWaves * gpad * lds_row_floats(head_size) * sizeof(float);
     return merge + (size_t)tbl_capacity * sizeof(int32_t);
 }
 

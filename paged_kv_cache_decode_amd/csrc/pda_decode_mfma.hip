@@ -131,9 +131,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // first, and a 4-byte aligned base made every 8- and 16-byte access of
     // the epilogue a misaligned one
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    float* red = smem;                                                       // [kWaves][8][D+2]
+    float* red = smem;  // [kWaves][HC][lds_row_floats(D)]: the unit epilogue's staging
     constexpr int HC = mfma_row_chunk(D);  // rows staged in LDS at a time
-    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * HC * (D + 2));
+    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * HC * lds_row_floats(D));
 
     // grid (Hkv, B, P): the partition index varies slowest (see the launcher)
     const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int c = 0; c < RC; ++c) {
             const int hi = 16 * c + c16 - h0;
             if (hi < 0 || hi >= hn) continue;
-            float* row = red + (wave * HC + hi) * (D + 2);
+            float* row = red + (wave * HC + hi) * lds_row_floats(D);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (4 * q4 + i >= CW) continue;  // repeated d-rows (D = 64)
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             for (int c = 0; c < RC; ++c) {
                 const int hi = 16 * c + c16 - h0;
                 if (hi < 0 || hi >= hn) continue;
-                float* row = red + (wave * HC + hi) * (D + 2);
+                float* row = red + (wave * HC + hi) * lds_row_floats(D);
                 row[D] = m[c];
                 row[D + 1] = l[c];
             }
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         __syncthreads();
         // the combine takes kHeadChunk rows per pass (one row per 32 threads)
         for (int r0 = 0; r0 < hn; r0 += kHeadChunk)
-            write_unit_rows<Elt, D>(p, red + r0 * (D + 2), HC, h0 + r0, min(kHeadChunk, hn - r0), b,
+            write_unit_rows<Elt, D, true>(p, red + r0 * lds_row_floats(D), HC, h0 + r0, min(kHeadChunk, hn - r0), b,
                                     g, part);
         if (h0 + HC < R) __syncthreads();  // before the next chunk reuses red
     }

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     // first, and a 4-byte aligned base made every 8- and 16-byte access of
     // the epilogue a misaligned one
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    float* red = smem;                                                  // [kWaves][GP][D+2]
-    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * (D + 2));
+    float* red = smem;  // [kWaves][GP][lds_row_floats(D)]: the unit epilogue's staging
+    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * GP * lds_row_floats(D));
 
     // grid (Hkv, B, P): the partition index varies slowest (see the launcher)
     const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     if (r == 0) {
 #pragma unroll
         for (int i = 0; i < GP; ++i) {
-            float* row = red + (wave * GP + i) * (D + 2);
+            float* row = red + (wave * GP + i) * lds_row_floats(D);
 #pragma unroll
             for (int e = 0; e < 8; ++e) row[c * 8 + e] = acc[i][e];
             if (c == 0) { row[D] = m[i]; row[D + 1] = l[i]; }
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     __syncthreads();
 
     // merge the wavefronts and write the unit's result
-    write_unit_rows<Elt, D>(p, red, GP, 0, R, b, g, part);
+    write_unit_rows<Elt, D, false>(p, red, GP, 0, R, b, g, part);
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);
 }
 

@@ -478,8 +478,12 @@ __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + 
 // (k < D/64), so a row's threads read 64 consecutive floats of LDS per pair
 // (8 consecutive elements per thread put threads 4 apart on the same banks)
 // and write 256 contiguous bytes of output or partials per pair and row.
-// All LDS reads of the step are issued before any arithmetic.
-template <typename Elt, int D>
+// All LDS reads of the step are issued before any arithmetic.  WT: partials
+// for the merge kernel are written through to the device coherence point
+// (device-scope stores), leaving no dirty L2 lines for the end of the launch
+// to write back (measured faster for the matrix-core kernel, slightly slower
+// for the VALU one).
+template <typename Elt, int D, bool WT>
 __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, int red_heads,
                                        int h0, int hn, int b, int g, int part) {
     constexpr int kTpr = 32;        // threads per row
@@ -492,7 +496,7 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
     float2 vw[kWaves][KP];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-        const float* rw = red + (w * red_heads + i) * (D + 2);
+        const float* rw = red + (w * red_heads + i) * lds_row_floats(D);
         mw[w] = rw[D];
         lw[w] = rw[D + 1];
 #pragma unroll
@@ -537,7 +541,7 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
         return;
     }
     const int64_t prow = row * p.num_partitions + part;
-    if (p.fused_merge) {  // read back by another workgroup of this launch
+    if (p.fused_merge || WT) {  // read back by another workgroup of this launch, or written through
         const int64_t row0 = row_index(p, b, g, 0);
         const int64_t span = (row_index(p, b, g, p.rows - 1) - row0 + 1) * p.num_partitions * D * 4;
         if (span < ((int64_t)1 << 31)) {
@@ -606,17 +610,17 @@ __device__ inline float2 load_coherent8(const float* base, uint32_t off) {
 #ifndef PDA_FUSED_ONE_TRIP
 #define PDA_FUSED_ONE_TRIP 1
 #endif
-// The fused merge in one memory round trip (up to kMergeUnroll partitions):
+
+// The fused merge in one memory round trip (up to U = kMergeUnroll partitions):
 // each thread takes four consecutive elements of one row and issues the
 // loads of every partition's (m, l) pair and of its four partial elements
 // together, then forms the weights itself (every thread of a row the same
 // ones): M = max over p, w_p = l_p 2^(m_p - M), the sums over p in index
 // order, times 1 / sum w_p -- the rule of merge_unit below, with no LDS
 // step and no barrier between the two kinds of loads.
-template <typename Elt, int D>
+template <typename Elt, int D, int U>
 __device__ inline void merge_unit_one_trip(const DecodeParams& p, int b, int g, int Pb) {
     constexpr int D4 = D / 4;
-    constexpr int U = kMergeUnroll;
     uint16_t* out16 = static_cast<uint16_t*>(p.out);
     const int R = p.rows, P = p.num_partitions;
     const int64_t row0 = row_index(p, b, g, 0);
@@ -784,9 +788,10 @@ __device__ inline void fused_merge_tail(const DecodeParams& p, const SeqRange& r
     const int64_t span = (row_index(p, b, g, p.rows - 1) - row_index(p, b, g, 0) + 1) *
                          p.num_partitions * D * 4;
     if (Pb <= kMergeUnroll && span < ((int64_t)1 << 31)) {
-        merge_unit_one_trip<Elt, D>(p, b, g, Pb);
+        merge_unit_one_trip<Elt, D, kMergeUnroll>(p, b, g, Pb);
         return;
     }
+
 #endif
     merge_unit<Elt, D>(p, b, g, Pb);
 }
