@@ -307,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int c = 0; c < RC; ++c) {
             float mt = fmaxf(fmaxf(sc[c][0], sc[c][1]), fmaxf(sc[c][2], sc[c][3]));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = max_xor<16>(mt);
+            mt = max_xor<32>(mt);
             mn[c] = fmaxf(m[c], mt);
             grew |= mn[c] > m[c];
         }
@@ -436,8 +436,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // full denominator of each lane row (all four lane groups hold the same m)
 #pragma unroll
     for (int c = 0; c < RC; ++c) {
-        l[c] += __shfl_xor(l[c], 16);
-        l[c] += __shfl_xor(l[c], 32);
+        l[c] = sum_xor<16>(l[c]);
+        l[c] = sum_xor<32>(l[c]);
     }
 
     // merge the wavefronts and write the unit's result, rows in chunks

@@ -252,14 +252,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     for (int x = LPT; x < kWave; x <<= 1) {
 #pragma unroll
         for (int i = 0; i < GP; ++i) {
-            const float mo = __shfl_xor(m[i], x);
-            const float lo = __shfl_xor(l[i], x);
+            // the partner lane's values: row swaps across 16-lane rows,
+            // a lane shuffle within a row
+            auto partner = [&](float v) {
+                return x == 16 ? xor_lane<16>(v) : x == 32 ? xor_lane<32>(v) : __shfl_xor(v, x);
+            };
+            const float mo = partner(m[i]);
+            const float lo = partner(l[i]);
             const float mm = fmaxf(m[i], mo);
             const float wa = fast_exp2(m[i] - mm), wb = fast_exp2(mo - mm);
             l[i] = l[i] * wa + lo * wb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float ao = __shfl_xor(acc[i][e], x);
+                const float ao = partner(acc[i][e]);
                 acc[i][e] = acc[i][e] * wa + ao * wb;
             }
             m[i] = mm;

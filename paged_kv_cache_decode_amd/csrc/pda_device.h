@@ -213,10 +213,50 @@ __device__ inline float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// ---- exchanges across the four 16-lane rows ------------------------------
+// gfx950's v_permlane16_swap / v_permlane32_swap exchange whole 16-lane rows
+// between two registers in the VALU, without the LDS round trip of a lane
+// shuffle (ds_bpermute).  With both operands x, the pair returned holds in
+// every lane x and the value of the lane X apart: first own and second the
+// partner's where (lane & X) == 0, the other way round elsewhere.
+struct RowPair {
+    float a, b;
+};
+template <int X>
+__device__ inline RowPair row_swap(float x) {
+    static_assert(X == 16 || X == 32, "row swaps exchange lanes 16 or 32 apart");
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (X == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return RowPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return RowPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+    }
+}
+// The value of lane (lane ^ X), X = 16 or 32.
+template <int X>
+__device__ inline float xor_lane(float x) {
+    const RowPair r = row_swap<X>(x);
+    return (threadIdx.x & X) == 0 ? r.b : r.a;
+}
+// max and sum over lanes l and l ^ X (the same value in both lanes; a sum is
+// own + partner, up to the order of two terms, which does not change it)
+template <int X>
+__device__ inline float max_xor(float x) {
+    const RowPair r = row_swap<X>(x);
+    return fmaxf(r.a, r.b);
+}
+template <int X>
+__device__ inline float sum_xor(float x) {
+    const RowPair r = row_swap<X>(x);
+    return r.a + r.b;
+}
+
 // Sum over aligned groups of N lanes (N in 2..64, power of two); every lane
 // of a group receives the group's sum.  Within a row the partner patterns are
 // xor 1, xor 2, then the half-row and row mirrors (which pair lane i with a
-// lane of the other quad / other half); across rows a lane shuffle.
+// lane of the other quad / other half); across rows the row swaps.
 template <int N>
 __device__ inline float group_sum(float x) {
     static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "group size");
@@ -224,8 +264,8 @@ __device__ inline float group_sum(float x) {
     if constexpr (N >= 4) x += dpp<kDppXor2>(x);
     if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
     if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    if constexpr (N >= 32) x = sum_xor<16>(x);
+    if constexpr (N >= 64) x = sum_xor<32>(x);
     return x;
 }
 
