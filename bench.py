@@ -128,11 +128,17 @@ def replicas_for(case):
     return reps, new_table.to(case.block_table.device), nb
 
 
+GRAPH_CALLS = 20  # decode calls captured into the graph of the graph pass
+
+
 def time_case(case, steps, warmup, passes=1):
     """Per-call device time from passes of plain back-to-back calls (two HIP
     events around the pass), and the split-KV kernel's own duration from
-    passes in which the library attaches events to that launch.  Returns a
-    dict with both, the plan and the last output."""
+    passes in which the library attaches events to that launch; then the
+    per-call time of GRAPH_CALLS calls captured once into a HIP graph and
+    replayed (as a serving loop runs its decode step), which leaves out the
+    host's per-call launch cost.  Returns a dict with these, the plan and the
+    last output (that of the last replay)."""
     import torch
     import kvgen
     import paged_kv_cache_decode_amd as pda
@@ -145,10 +151,10 @@ def time_case(case, steps, warmup, passes=1):
                      device=case.q.device)
     pda.paged_decode_attn_workspace_init(ws)
 
-    def call(i, e0=None, e1=None):
+    def call(i, e0=None, e1=None, stream=None):
         kc, vc = reps[i % R]
         pda.paged_decode_attn_timed(shape, plan, case.q, kc, vc, table,
-                                    case.seq_lens_t, case.scale, out, ws, e0, e1)
+                                    case.seq_lens_t, case.scale, out, ws, e0, e1, stream)
 
     # every replica pool is touched at least twice before timing (a pool's
     # first use in a process pays for page-table and TLB set-up)
@@ -183,10 +189,35 @@ def time_case(case, steps, warmup, passes=1):
     order = sorted(range(passes), key=lambda k: calls[k]["call_ms"])
     med = order[len(order) // 2]
     kv = case.kv_bytes()
+    # graph pass: capture on a side stream after a warm-up there, replay
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(GRAPH_CALLS):
+            call(i, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(GRAPH_CALLS):
+            call(i, stream=side)
+    for _ in range(2):
+        graph.replay()
+    replays = max(2, steps // GRAPH_CALLS)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(stop) / (replays * GRAPH_CALLS)
+    del graph
     return dict(out=out, plan=plan, replicas=R, passes=calls, call_ms=calls[med]["call_ms"],
                 wall_ms=calls[med]["wall_ms"], best_call_ms=calls[order[0]]["call_ms"],
                 kernel_ms=sorted(kernels)[len(kernels) // 2], kernel_passes=kernels,
-                kv_bytes=kv)
+                graph_ms=graph_ms, kv_bytes=kv)
 
 
 def summary(name, case, r):
@@ -203,6 +234,7 @@ def summary(name, case, r):
             "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
             "kernel_GBps": round(kgbs, 1), "kernel_pct_of_peak": round(100 * kgbs / PEAK_GBS, 2),
             "us_per_context_token": round(us / sum(case.seq_lens), 6),
+            "graph_us_per_call": round(r["graph_ms"] * 1e3, 3),
             "variant": {1: "valu", 2: "mfma"}.get(r["plan"].variant, "?"),
             "merge": {0: "fused", 1: "kernel"}.get(r["plan"].merge, "?"),
             "replica_pools": r["replicas"],
@@ -313,7 +345,31 @@ def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 20
         us = per_launch_us(mib << 20, 256)
         same[f"{mib}MiB_256wg"] = {"us_per_launch": round(us, 3),
                                    "GBps": round((mib << 20) / (us * 1e-6) / 1e9, 1)}
-    floor_us = per_launch_us(16, 1, n=1000)
+    # the launch floor: 100 16-byte reads by one workgroup captured into a
+    # graph and replayed, so that the host's per-launch cost (more than the
+    # device's through the Python binding) is not what is timed
+    tiny = src[:16]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pda.pda_read_probe(tiny, sink, 1, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for _ in range(100):
+            pda.pda_read_probe(tiny, sink, 1, stream=side)
+    graph.replay()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    floor_us = a.elapsed_time(b) / 1000 * 1e3
+    del graph
     del src
     torch.cuda.empty_cache()
     best = max(rates, key=rates.get)
@@ -326,7 +382,8 @@ def read_probe(nbytes: int = 4 << 30, calls: int = 10, grids=(256, 512, 1024, 20
             "launch_floor_us": round(floor_us, 3),
             "what_same_bytes": "back-to-back reads of 128 MiB and 64 MiB slices of the buffer "
                                "(rotating, so none is served by the MALL) by 256 workgroups, "
-                               "per launch; launch floor: a 16-byte read by one workgroup"}
+                               "per launch; launch floor: a 16-byte read by one workgroup, "
+                               "per launch from a graph of 100"}
 
 
 def cpu_identity() -> dict:
@@ -400,16 +457,17 @@ def render_table(line: dict) -> str:
     if line.get("parity") is not None:
         rows[0] = dict(rows[0], parity=line["parity"])
     out = ["| workload | variant | merge | P x T_p | us/call | % of 8 TB/s | split-KV kernel us "
-           "(% peak) | rel-Linf (worst seq) | non-finite |",
-           "|---|---|---|---|---|---|---|---|---|"]
+           "(% peak) | graph us/call | rel-Linf (worst seq) | non-finite |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         par = r.get("parity")
         ptxt = "-" if par is None else f"{par['rel_linf']:.2e} ({par['rel_linf_worst_seq']:.2e})"
         ntxt = "-" if par is None else str(par["nonfinite"])
+        gtxt = "-" if r.get("graph_us_per_call") is None else f"{r['graph_us_per_call']:.2f}"
         out.append(f"| {r['workload']} | {r['variant']} | {r['merge']} | {r['P']} x {r['T_p']} | "
                    f"{r['us_per_call']:.2f} | {r['pct_of_peak']:.1f} % | "
-                   f"{r['splitkv_kernel_us']:.2f} ({r['kernel_pct_of_peak']:.1f} %) | {ptxt} | "
-                   f"{ntxt} |")
+                   f"{r['splitkv_kernel_us']:.2f} ({r['kernel_pct_of_peak']:.1f} %) | {gtxt} | "
+                   f"{ptxt} | {ntxt} |")
     slopes = {k: v for k, v in line.get("extra", {}).items() if not isinstance(v, dict)}
     for k, v in slopes.items():
         out.append(f"\n{k}: {v}")
