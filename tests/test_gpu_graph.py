@@ -111,3 +111,36 @@ def test_graph_with_workspace_init_and_fused_merge():
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), bits(eager)), f"replay {rep}"
+
+
+def test_default_stream_follows_torch_current_stream():
+    """With no stream argument the binding launches on torch's current stream
+    (read as a raw handle): the default stream outside a stream context, the
+    context's stream inside one; a capture then needs no stream argument."""
+    assert pda._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert pda._stream(None) == side.cuda_stream
+    assert pda._stream(None) == torch.cuda.current_stream().cuda_stream
+    case = configs.cfg1(device="cuda")
+    shape = pda.make_shape(**kvgen.shape_dict(case))
+    plan = pda.paged_decode_attn_plan(shape)
+    ws = torch.zeros(max(1, pda.pda_workspace_bytes(shape, plan)), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(case.q)
+    _call(case, out, ws, plan, None)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _call(case, out, ws, plan, None)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        _call(case, out, ws, plan, None)
+    out.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(eager))
