@@ -17,8 +17,9 @@
 //         four lanes that hold that head; the accumulator is rescaled only
 //         when some max grew.
 //   PV    O^T = V^T P^T on v_mfma_f32_16x16x16_{bf16,f16}, one MFMA per
-//         element e of the lanes' 8-element V chunks: round r of V loads
-//         token 4(l/16) + r, elements d = 8*(l%16) + e, so element e of the
+//         element e of the lanes' VE-element V chunks (VE = 8, or 4 at head
+//         size 64 so that the 16 d-rows stay distinct): round r of V loads
+//         token 4(l/16) + r, elements d = VE*(l%16) + e, so element e of the
 //         lane's four rounds is exactly its A operand (d-row l%16, tokens
 //         4(l/16) .. +4), and the exp'd scores the lane holds (row l%16,
 //         the same four tokens) are exactly its B operand.  Neither V nor P
@@ -33,8 +34,9 @@
 // then holds 16 elements, d = 64*s2 + 16*q4 .. +16, decoded exactly to the
 // 16-bit type as the A operands of k-steps 2*s2 and 2*s2 + 1; the query
 // elements of each k-step are loaded in the same permuted order of d (a dot
-// product does not depend on the order of its terms).  V chunks are 8-byte
-// loads decoded to fp32.  k_scale is folded into the score scale and v_scale
+// product does not depend on the order of its terms).  V chunks are VE-byte
+// loads, byte-transposed across the four rounds and decoded exactly to the
+// 16-bit type.  k_scale is folded into the score scale and v_scale
 // into the output (write_unit_rows).
 //
 // Compiled once per (element type, head size, KV type): PDA_DTYPE (0 bf16,
@@ -105,10 +107,34 @@ struct MfmaPV<FP16> {
     }
 };
 
-// 32-bit word i of a 16-byte chunk (i a compile-time constant after unrolling)
+// 32-bit word i of a 16- or 8-byte chunk (i a compile-time constant after
+// unrolling)
 __device__ inline uint32_t word_of(const uint4& v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
+__device__ inline uint32_t word_of(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+
+// A lane's V chunk of one round: VE elements, 16, 8 or 4 bytes
+template <int BYTES>
+struct VChunk;
+template <>
+struct VChunk<16> {
+    typedef uint4 type;
+    __device__ static type load(const char* p) { return load_row16(p); }
+    __device__ static type load_buf(const char* b, uint32_t off, bool v) { return load_row16_buf(b, off, v); }
+};
+template <>
+struct VChunk<8> {
+    typedef uint2 type;
+    __device__ static type load(const char* p) { return load_row8(p); }
+    __device__ static type load_buf(const char* b, uint32_t off, bool v) { return load_row8_buf(b, off, v); }
+};
+template <>
+struct VChunk<4> {
+    typedef uint32_t type;
+    __device__ static type load(const char* p) { return load_row4(p); }
+    __device__ static type load_buf(const char* b, uint32_t off, bool v) { return load_row4_buf(b, off, v); }
+};
 
 // The element type and head size are template parameters of the kernel so
 // that every instantiation has its own symbol across translation units.
@@ -120,13 +146,14 @@ template <typename Elt, int D, bool ALIGNED, bool BUF, int RC, bool F8>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(RC == 1 || RC == 2, "one or two 16-row chunks");
     using Geo = MfmaGeom<D>;
-    constexpr int KS = Geo::KS, DH = Geo::DH, CW = Geo::CW, TT = 16;
+    constexpr int KS = Geo::KS, DH = Geo::DH, VE = Geo::VE, TT = 16;
     constexpr int EB = F8 ? 1 : 2;             // KV bytes per element
     // tiles in register buffers (fp8 tiles are half the bytes and registers)
     constexpr int S = F8 ? PDA_MFMA_STAGES_FP8 : PDA_MFMA_STAGES;
     static_assert(S >= 2 && S <= 6, "stages");
     constexpr int KL = F8 ? KS / 2 : KS;       // 16-byte K loads per lane and tile
-    using VRaw = typename std::conditional<F8, uint2, uint4>::type;  // 8 V elements
+    using VC = VChunk<VE * EB>;
+    using VRaw = typename VC::type;            // a lane's VE V elements of one round
     // 16-byte aligned: the static LDS of the merge tail (4228 bytes) comes
     // first, and a 4-byte aligned base made every 8- and 16-byte access of
     // the epilogue a misaligned one
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const char* vc = static_cast<const char*>(p.v_cache);
     const int64_t head_off = (int64_t)g * p.head_stride;               // elements
     const uint32_t k_lane = (uint32_t)(16 * q4);                        // bytes
-    const uint32_t v_lane = (uint32_t)(8 * (c16 % CW)) * EB;            // bytes
+    const uint32_t v_lane = (uint32_t)(VE * c16 * EB);                  // bytes
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
     // Tile jj >= ntiles is a prefetch past the end: with buffer loads (BUF)
@@ -240,29 +267,23 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 EB * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
             const uint32_t off = (uint32_t)dt * (EB * D) + v_lane;
 #pragma unroll
-            for (int dh = 0; dh < DH; ++dh) {
-                if constexpr (F8)
-                    vr[r][dh] = kBuf ? load_row8_buf(vc + base, off + 128 * dh, valid)
-                                     : load_row8(vc + base + off + 128 * dh);
-                else
-                    vr[r][dh] = kBuf ? load_row16_buf(vc + base, off + 256 * dh, valid)
-                                     : load_row16(vc + base + off + 256 * dh);
-            }
+            for (int dh = 0; dh < DH; ++dh)
+                vr[r][dh] = kBuf ? VC::load_buf(vc + base, off + 128 * EB * dh, valid)
+                                 : VC::load(vc + base + off + 128 * EB * dh);
         }
     };
     auto block_of = [&](int jj) {
         return ALIGNED ? tile_block(p, trow, tile_start(jj)) : TileBlock{0, 0};
     };
 
-    // oacc[c][dh][e][i] = O[row 16c + c16][d = dh*128 + 8*(4*q4 + i) + e]
-    // (for D = 64 the d-rows 4*q4 + i >= CW repeat the first CW)
-    f32x4_t oacc[RC][DH][8];
+    // oacc[c][dh][e][i] = O[row 16c + c16][d = dh*128 + VE*(4*q4 + i) + e]
+    f32x4_t oacc[RC][DH][VE];
 #pragma unroll
     for (int a = 0; a < RC; ++a)
 #pragma unroll
         for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[a][dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int e = 0; e < VE; ++e) oacc[a][dh][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m[RC], l[RC];
 #pragma unroll
     for (int c = 0; c < RC; ++c) {
@@ -321,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
                 for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) oacc[c][dh][e] *= alpha;
+                    for (int e = 0; e < VE; ++e) oacc[c][dh][e] *= alpha;
                 m[c] = mn[c];
             }
         }
@@ -347,45 +368,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
                 // byte e of the four rounds (tokens 4*q4 + r, in order) into
                 // one word, which two packed conversions turn into the A
                 // operand of element e
-                uint32_t tb[8];
-                byte_transpose4(vr[0][dh].x, vr[1][dh].x, vr[2][dh].x, vr[3][dh].x,
-                                *reinterpret_cast<uint32_t(*)[4]>(&tb[0]));
-                byte_transpose4(vr[0][dh].y, vr[1][dh].y, vr[2][dh].y, vr[3][dh].y,
-                                *reinterpret_cast<uint32_t(*)[4]>(&tb[4]));
+                uint32_t tb[VE];
+                if constexpr (VE == 8) {
+                    byte_transpose4(vr[0][dh].x, vr[1][dh].x, vr[2][dh].x, vr[3][dh].x,
+                                    *reinterpret_cast<uint32_t(*)[4]>(&tb[0]));
+                    byte_transpose4(vr[0][dh].y, vr[1][dh].y, vr[2][dh].y, vr[3][dh].y,
+                                    *reinterpret_cast<uint32_t(*)[4]>(&tb[4]));
+                } else {
+                    byte_transpose4(vr[0][dh], vr[1][dh], vr[2][dh], vr[3][dh],
+                                    *reinterpret_cast<uint32_t(*)[4]>(&tb[0]));
+                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < VE; ++e) {
                     const uint2 a = make_uint2(fp8x2_to_16bit<Elt, false>(tb[e]),
                                                fp8x2_to_16bit<Elt, true>(tb[e]));
 #pragma unroll
                     for (int c = 0; c < RC; ++c)
                         oacc[c][dh][e] = MfmaPV<Elt>::run(a, pb[c], oacc[c][dh][e]);
                 }
-                continue;
-            }
-            // the lane's four V rounds (tokens 4*q4 + r) as 16-bit elements
-            uint4 w[4];
+            } else {
+                // A operand: element e of the lane's four V rounds (tokens
+                // 4*q4 + r), tokens in order
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (F8)
-                    w[r] = fp8x8_to_16bit<Elt>(vr[r][dh].x, vr[r][dh].y);
-                else
-                    w[r] = vr[r][dh];
-            }
+                for (int e = 0; e < VE; ++e) {
+                    const int wi = e / 2;
+                    uint2 a;
+                    if (e % 2 == 0) {
+                        a.x = (word_of(vr[0][dh], wi) & 0xffffu) | (word_of(vr[1][dh], wi) << 16);
+                        a.y = (word_of(vr[2][dh], wi) & 0xffffu) | (word_of(vr[3][dh], wi) << 16);
+                    } else {
+                        a.x = (word_of(vr[0][dh], wi) >> 16) | (word_of(vr[1][dh], wi) & 0xffff0000u);
+                        a.y = (word_of(vr[2][dh], wi) >> 16) | (word_of(vr[3][dh], wi) & 0xffff0000u);
+                    }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // A operand: element e of the four rounds, tokens in order
-                const int wi = e / 2;
-                uint2 a;
-                if (e % 2 == 0) {
-                    a.x = (word_of(w[0], wi) & 0xffffu) | (word_of(w[1], wi) << 16);
-                    a.y = (word_of(w[2], wi) & 0xffffu) | (word_of(w[3], wi) << 16);
-                } else {
-                    a.x = (word_of(w[0], wi) >> 16) | (word_of(w[1], wi) & 0xffff0000u);
-                    a.y = (word_of(w[2], wi) >> 16) | (word_of(w[3], wi) & 0xffff0000u);
+                    for (int c = 0; c < RC; ++c)
+                        oacc[c][dh][e] = MfmaPV<Elt>::run(a, pb[c], oacc[c][dh][e]);
                 }
-#pragma unroll
-                for (int c = 0; c < RC; ++c)
-                    oacc[c][dh][e] = MfmaPV<Elt>::run(a, pb[c], oacc[c][dh][e]);
             }
         }
     };
@@ -449,14 +467,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             if (hi < 0 || hi >= hn) continue;
             float* row = red + (wave * HC + hi) * lds_row_floats(D);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (4 * q4 + i >= CW) continue;  // repeated d-rows (D = 64)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int dh = 0; dh < DH; ++dh)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        row[dh * 128 + 8 * (4 * q4 + i) + e] = oacc[c][dh][e][i];
-            }
+                    for (int e = 0; e < VE; ++e)
+                        row[dh * 128 + VE * (4 * q4 + i) + e] = oacc[c][dh][e][i];
         }
         if (q4 == 0) {
 #pragma unroll

@@ -153,6 +153,25 @@ __device__ inline uint2 load_row8_buf(const char* base, uint32_t off, bool valid
     return make_uint2(v.x, v.y);
 }
 
+// 4 bytes of a row (an fp8 V chunk at head size 64), plain and through a
+// buffer resource (same contract as load_row16 / load_row16_buf).
+__device__ inline uint32_t load_row4(const char* ptr) {
+#if PDA_VALU_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ptr));
+#else
+    return *reinterpret_cast<const uint32_t*>(ptr);
+#endif
+}
+__device__ inline uint32_t load_row4_buf(const char* base, uint32_t off, bool valid) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base), (short)0, valid ? 0x7fffffff : 0, kBufferWord3);
+#if PDA_VALU_NT
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 2);  // nt
+#else
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, 0);
+#endif
+}
+
 // Device-scope (all XCDs) store and load of fp32 workspace data: the store
 // is written through to the device coherence point (sc1), the load reads
 // from it, so partials written by one workgroup can be read by another on a
@@ -496,13 +515,14 @@ __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, i
 // A 16-token tile.  K rows feed the A operand of v_mfma_f32_16x16x32 (S^T =
 // K Q^T): lane l reads token l%16, elements 32s + 8(l/16) .. +8 for k-step s.
 // V rows feed the A operand of v_mfma_f32_16x16x16 (O^T = V^T P^T): for
-// round r lane l reads token 4(l/16) + r, elements dh*128 + 8*(l%16 % CW) .. +8,
-// CW = min(16, D/8) column groups per 128-wide half dh.
+// round r lane l reads token 4(l/16) + r, elements dh*128 + VE*(l%16) .. +VE,
+// VE = 8 (16 lanes cover a 128-wide half dh) or 4 at D 64 (16 lanes cover
+// the row), so the 16 d-rows of every PV product are distinct columns.
 template <int D>
 struct MfmaGeom {
     static constexpr int KS = D / 32;                 // QK k-steps (16-byte K loads per tile)
     static constexpr int DH = D >= 128 ? D / 128 : 1; // 128-wide halves of V
-    static constexpr int CW = D >= 128 ? 16 : D / 8;  // distinct column groups per half
+    static constexpr int VE = D >= 128 ? 8 : 4;       // V elements per lane and round
 };
 __device__ inline int mfma_k_offset(int lane) { return lane & 15; }
 __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + r; }
