@@ -43,3 +43,27 @@ def test_traffic_summary_is_keyed_to_kernel_and_sources():
     same = t["kernel_source_sha256"] == bench.kernel_source_hash(t["variant"])
     got = bench.measured_traffic(t["variant"])
     assert (got == t["hbm_bytes_per_launch"]) if same else (got is None)
+
+
+def test_design_table_is_the_stored_bench_line():
+    """The results table in the design doc is printed from the stored bench line
+    (profiles/bench_full.json) by `bench.py --table`, not typed by hand: the
+    rendered table appears in the document verbatim."""
+    r = _run(["--table", os.path.join(ROOT, "profiles", "bench_full.json")])
+    assert r.returncode == 0, r.stderr
+    table = r.stdout.strip()
+    assert table.startswith("| workload |")
+    with open(os.path.join(ROOT, "DESIGN.md")) as f:
+        design = f.read()
+    assert table in design
+
+
+def test_table_renders_rows_without_newer_keys():
+    """A stored line from before a column existed still renders ('-')."""
+    sys.path.insert(0, ROOT)
+    import bench
+    row = {"workload": "w", "variant": "mfma", "merge": "kernel", "P": 2, "T_p": 16,
+           "us_per_call": 1.0, "pct_of_peak": 1.0, "splitkv_kernel_us": 1.0,
+           "kernel_pct_of_peak": 1.0}
+    out = bench.render_table({"headline": row, "parity": None, "extra": {}})
+    assert out.splitlines()[2] == "| w | mfma | kernel | 2 x 16 | 1.00 | 1.0 % | 1.00 (1.0 %) | - | - | - |"
