@@ -21,6 +21,7 @@ Prints ONE JSON line.  Options: --gpus (1 only), --steps, --warmup,
 --cpu-seconds (oracle baseline budget), --no-extra (skip the other shapes).
 """
 import argparse
+import subprocess
 import json
 import math
 import os
@@ -474,6 +475,36 @@ def render_table(line: dict) -> str:
     return "\n".join(out)
 
 
+def extra_specs():
+    """The extra rows: (name, maker) for every config shape, ladder point and
+    next-row workload timed after the headline."""
+    from kvgen import configs
+    L = 32768
+    specs = [(f"cfg2 Hq{hq} 32K", lambda hq=hq: configs.cfg2(hq, L, device="cuda"))
+             for hq in (8, 16, 24)]
+    specs += [(f"cfg2 Hq32 {n}", lambda n=n: configs.cfg2(32, n, device="cuda"))
+              for n in configs.CFG2_LENS]
+    specs += [("cfg3 B1 bf16 32K", lambda: configs.cfg3(1, L, device="cuda")),
+              ("cfg3 B1 fp16 32K", lambda: configs.cfg3(1, L, dtype="fp16", device="cuda")),
+              ("cfg3 B8 bf16 32K", lambda: configs.cfg3(8, L, device="cuda"))]
+    specs += [(f"cfg4 {n}", lambda n=n: configs.cfg4(n, device="cuda"))
+              for n in configs.CFG4_LENS]
+    specs += [("cfg5 B64 mixed", lambda: configs.cfg5(device="cuda"))]
+    specs += [(f"cfg3 sliding W1024 B{b} 32K", lambda b=b: configs.cfg3_sliding(b, L, device="cuda"))
+              for b in (1, 8)]
+    specs += [("cfg4 TP2 share 12/2 32K", lambda: configs.cfg4_tp2(L, device="cuda"))]
+    specs += [("headline fp8 KV 32K", lambda: configs.cfg2(32, L, device="cuda", kv_dtype="fp8")),
+              ("cfg3 B8 fp8 KV 32K", lambda: configs.cfg3(8, L, device="cuda", kv_dtype="fp8")),
+              ("cfg4 fp8 KV 32K", lambda: configs.cfg4(L, device="cuda", kv_dtype="fp8")),
+              ("cfg5 B64 mixed fp8 KV", lambda: configs.cfg5(device="cuda", kv_dtype="fp8"))]
+    specs += [("headline q_len 4 32K", lambda: configs.cfg2(32, L, device="cuda", q_len=4)),
+              ("cfg3 B8 q_len 4 32K", lambda: configs.cfg3(8, L, device="cuda", q_len=4)),
+              ("cfg5 B64 mixed q_len 2", lambda: configs.cfg5(device="cuda", q_len=2))]
+    specs += [(f"cfg3 TP2 share 16/8 B{b} 32K", lambda b=b: configs.cfg3_tp2(b, L, device="cuda"))
+              for b in (1, 8)]
+    return specs
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -490,6 +521,9 @@ def main():
                     help="print the markdown table of a stored bench line and exit")
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS),
                     help="the timed workload (default: the headline one)")
+    ap.add_argument("--row", metavar="NAME",
+                    help="time one extra row in this process and print its summary line "
+                         "(the full run starts one such process per row)")
     args = ap.parse_args()
     if args.table:
         with open(args.table) as f:
@@ -503,15 +537,26 @@ def main():
 
     import numpy as np
     import torch
-    import oracle
     import paged_kv_cache_decode_amd as pda
     from kvgen import configs
 
     torch.cuda.set_device(0)
     pda.load_library()
+    if args.row:
+        makers = dict(extra_specs())
+        if args.row not in makers:
+            print(f"no extra row named {args.row!r}", file=sys.stderr)
+            sys.exit(2)
+        log(f"timing {args.row}")
+        c = makers[args.row]()
+        rr = time_case(c, args.steps, args.warmup, passes=args.passes)
+        row = summary(args.row, c, rr)
+        if not args.no_parity:
+            row["parity"] = score(c, rr["out"])
+        print(json.dumps(row), flush=True)
+        return
     log(f"library: {pda.pda_build_id()}")
 
-    L = 32768
     wl = WORKLOADS[args.workload]
     case = wl["make"]()
     log(f"timing workload {args.workload}: {wl['desc']}")
@@ -525,40 +570,28 @@ def main():
         ref, cpu = cpu_baseline(case, args.cpu_seconds)
         parity = score(case, r["out"], ref)
 
+    kbytes = r["kv_bytes"]
+    call_ms, kernel_ms = r["call_ms"], r["kernel_ms"]
+    desc_case = dict(B=case.B, max_seq_len=case.max_seq_len)
+    del case, r
+    torch.cuda.empty_cache()
+
     extra = {}
     if not args.no_extra:
         small_steps = max(20, args.steps // 4)
-        specs = [(f"cfg2 Hq{hq} 32K", lambda hq=hq: configs.cfg2(hq, L, device="cuda"))
-                 for hq in (8, 16, 24)]
-        specs += [(f"cfg2 Hq32 {n}", lambda n=n: configs.cfg2(32, n, device="cuda"))
-                  for n in configs.CFG2_LENS]
-        specs += [("cfg3 B1 bf16 32K", lambda: configs.cfg3(1, L, device="cuda")),
-                  ("cfg3 B1 fp16 32K", lambda: configs.cfg3(1, L, dtype="fp16", device="cuda")),
-                  ("cfg3 B8 bf16 32K", lambda: configs.cfg3(8, L, device="cuda"))]
-        specs += [(f"cfg4 {n}", lambda n=n: configs.cfg4(n, device="cuda"))
-                  for n in configs.CFG4_LENS]
-        specs += [("cfg5 B64 mixed", lambda: configs.cfg5(device="cuda"))]
-        specs += [(f"cfg3 sliding W1024 B{b} 32K", lambda b=b: configs.cfg3_sliding(b, L, device="cuda"))
-                  for b in (1, 8)]
-        specs += [("cfg4 TP2 share 12/2 32K", lambda: configs.cfg4_tp2(L, device="cuda"))]
-        specs += [("headline fp8 KV 32K", lambda: configs.cfg2(32, L, device="cuda", kv_dtype="fp8")),
-                  ("cfg3 B8 fp8 KV 32K", lambda: configs.cfg3(8, L, device="cuda", kv_dtype="fp8")),
-                  ("cfg4 fp8 KV 32K", lambda: configs.cfg4(L, device="cuda", kv_dtype="fp8")),
-                  ("cfg5 B64 mixed fp8 KV", lambda: configs.cfg5(device="cuda", kv_dtype="fp8"))]
-        specs += [("headline q_len 4 32K", lambda: configs.cfg2(32, L, device="cuda", q_len=4)),
-                  ("cfg3 B8 q_len 4 32K", lambda: configs.cfg3(8, L, device="cuda", q_len=4)),
-                  ("cfg5 B64 mixed q_len 2", lambda: configs.cfg5(device="cuda", q_len=2))]
-        specs += [(f"cfg3 TP2 share 16/8 B{b} 32K", lambda b=b: configs.cfg3_tp2(b, L, device="cuda"))
-                  for b in (1, 8)]
-        for name, mk in specs:
-            log(f"timing {name}")
-            c = mk()
-            rr = time_case(c, small_steps, max(5, args.warmup // 4), passes=3)
-            extra[name] = summary(name, c, rr)
-            if not args.no_parity:
-                extra[name]["parity"] = score(c, rr["out"])
-            del c, rr
-            torch.cuda.empty_cache()
+        # each row in a process of its own: a row's pools are then its
+        # process's first allocation, as a serving KV cache is, instead of
+        # landing in memory that earlier rows freed (measured 4-6 % slower
+        # per call on the 32K rows)
+        for name, _ in extra_specs():
+            cmd = [sys.executable, os.path.abspath(__file__), "--row", name,
+                   "--steps", str(small_steps), "--warmup", str(max(5, args.warmup // 4)),
+                   "--passes", "3"] + (["--no-parity"] if args.no_parity else [])
+            res = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+            if res.returncode != 0:
+                log(f"row {name!r} failed (exit {res.returncode})")
+                sys.exit(1)
+            extra[name] = json.loads(res.stdout.strip().splitlines()[-1])
         # decode time added per token of context: the slope of us/call over each ladder
         def slope(points):
             xs = np.array([a for a, _ in points], dtype=np.float64)
@@ -570,8 +603,7 @@ def main():
         extra["headline slope us per context token"] = slope(
             [(n, extra[f"cfg2 Hq32 {n}"]["us_per_call"]) for n in configs.CFG2_LENS])
 
-    kbytes = r["kv_bytes"]
-    achieved = kbytes / (r["kernel_ms"] * 1e-3) / 1e9
+    achieved = kbytes / (kernel_ms * 1e-3) / 1e9
     probe = None
     if not args.no_probe:
         log("timing the streaming-read probe")
@@ -584,13 +616,14 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["call_ms"], 6),
+        "ms_per_step": round(call_ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["desc"], "global_batch": case.B, "seq_len": case.max_seq_len,
+        "config": {"workload": wl["desc"], "global_batch": desc_case["B"],
+                   "seq_len": desc_case["max_seq_len"],
                    "parallelism": "single GPU"},
         "us_per_call": head["us_per_call"],
         "pct_of_peak": head["pct_of_peak"],
@@ -603,7 +636,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": measured_traffic(head["variant"]),
-                     "kernel_us": round(r["kernel_ms"] * 1e3, 3),
+                     "kernel_us": round(kernel_ms * 1e3, 3),
                      "call_frac": round(head["GBps"] / PEAK_GBS, 4),
                      "call_us": head["us_per_call"],
                      "algorithmic_bytes_per_launch": kbytes},
