@@ -111,9 +111,10 @@ hipError_t launch_merge(int dtype, int head_size, const DecodeParams& p, int bat
                         hipStream_t stream);
 // zero `bytes` at device pointer `dst` with a fill kernel on `stream`
 hipError_t launch_zero_fill(void* dst, int64_t bytes, hipStream_t stream);
-// rows: 0 = the VALU kernel's rows, 1 = the MFMA kernel's K rows, 2 = its V rows
-hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
-                        hipStream_t stream);
+// rows: 0 = the VALU kernel's rows, 1 = the MFMA kernel's K rows, 2 = its V
+// rows; kv_elt_bytes (1 for fp8 KV, else 2) sets the MFMA K rows' lane map
+hipError_t launch_trace(int head_size, int kv_elt_bytes, bool aligned, int rows,
+                        const DecodeParams& p, int batch, hipStream_t stream);
 
 // The decode step behind every decode entry point: validates the shape and
 // plan, lays the plan's workspace out in `workspace` (workspace_bytes long),
@@ -138,9 +139,32 @@ __host__ __device__ constexpr int mfma_row_chunk(int head_size) {
     return head_size <= 128 ? 16 : kHeadChunk;
 }
 
-// Bytes of dynamic LDS the MFMA kernel uses (rows staged mfma_row_chunk at a time).
-inline size_t mfma_lds_bytes(int head_size, int tbl_capacity) {
-    return (size_t)kWaves * mfma_row_chunk(head_size) * lds_row_floats(head_size) * sizeof(float) +
+// Whether the MFMA kernel loads K in whole rows and moves each tile through
+// an LDS buffer into the matrix-core operand layout (otherwise it loads the
+// operand layout directly: 64 bytes of each of 16 rows per instruction).  By
+// measurement: whole rows at head sizes 64 and 256, for fp8 KV, and for
+// partitions of at most 512 tokens (a call's first loads are then a large
+// part of it); the direct loads for 16-bit KV at head size 128 with longer
+// partitions, where the LDS round trip measured 0.25 us slower per call.
+__host__ __device__ inline bool mfma_k_whole_rows(int head_size, int kv_elt_bytes,
+                                                  int tokens_per_part) {
+    return head_size != 128 || kv_elt_bytes != 2 || tokens_per_part <= 512;
+}
+
+// Bytes of the MFMA kernel's per-wave LDS buffers through which a K tile
+// moves from whole-row loads into the matrix-core operand layout: 16 rows of
+// kv_elt_bytes * head_size bytes, each padded by 16 bytes.
+__host__ __device__ constexpr int mfma_kstage_bytes(int head_size, int kv_elt_bytes) {
+    return kWaves * 16 * (kv_elt_bytes * head_size + 16);
+}
+
+// Bytes of dynamic LDS the MFMA kernel uses: the K staging buffers (whole-row
+// K loads only), the epilogue's rows (staged mfma_row_chunk at a time), the
+// block-table slice.
+inline size_t mfma_lds_bytes(int head_size, int kv_elt_bytes, bool k_whole_rows,
+                             int tbl_capacity) {
+    return (size_t)(k_whole_rows ? mfma_kstage_bytes(head_size, kv_elt_bytes) : 0) +
+           (size_t)kWaves * mfma_row_chunk(head_size) * lds_row_floats(head_size) * sizeof(float) +
            (size_t)tbl_capacity * sizeof(int32_t);
 }
 

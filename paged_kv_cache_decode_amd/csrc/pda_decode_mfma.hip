@@ -7,9 +7,13 @@
 // rows padded to 16 per chunk:
 //
 //   QK^T  S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: a 16-token tile of K
-//         rows is the A operand (lane l loads 16 bytes of token l%16), Q^T the
-//         B operand.  The 16x16 result leaves each lane the scores of one
-//         row (l%16) for four tokens (4(l/16) + r, r = 0..3).
+//         rows is the A operand (lane l holds 16 bytes of token l%16 per
+//         k-step), Q^T the B operand.  K is loaded in whole rows (each load
+//         instruction reads whole 128-byte lines, where the operand layout
+//         would read 64 bytes of each of 16 rows) and moved into the operand
+//         layout through the wave's own LDS buffer.  The 16x16 result leaves
+//         each lane the scores of one row (l%16) for four tokens (4(l/16) +
+//         r, r = 0..3).
 //   mask  scores of tokens at or past the partition end, outside a sliding
 //         window or after the row's causal end become -inf by select; tail
 //         slots and slots before a window are never addressed (see tile_row).
@@ -142,7 +146,7 @@ struct VChunk<4> {
 // are packed in RC chunks of 16 (RC = 2 for R > 16): each K tile feeds RC
 // QK and RC PV products, and each chunk keeps its own softmax state and
 // accumulators.
-template <typename Elt, int D, bool ALIGNED, bool BUF, int RC, bool F8>
+template <typename Elt, int D, bool ALIGNED, bool BUF, int RC, bool F8, bool KWR>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(RC == 1 || RC == 2, "one or two 16-row chunks");
     using Geo = MfmaGeom<D>;
@@ -158,9 +162,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // first, and a 4-byte aligned base made every 8- and 16-byte access of
     // the epilogue a misaligned one
     extern __shared__ __attribute__((aligned(16))) float smem[];
-    float* red = smem;  // [kWaves][HC][lds_row_floats(D)]: the unit epilogue's staging
+    // K rows: RB bytes, LPT lanes per row in a whole-row load, staged KSB apart
+    constexpr int RB = EB * D, LPT = RB / 16, KSB = RB + 16;
+    constexpr int KSTAGE = KWR ? mfma_kstage_bytes(D, EB) : 0;
+    static_assert(KSTAGE % 16 == 0, "the epilogue rows stay 16-byte aligned");
+    char* kst = reinterpret_cast<char*>(smem);  // [kWaves][16][KSB]: each wave's K tile (KWR)
+    float* red = smem + KSTAGE / 4;  // [kWaves][HC][lds_row_floats(D)]: the epilogue's rows
     constexpr int HC = mfma_row_chunk(D);  // rows staged in LDS at a time
-    int32_t* tbl = reinterpret_cast<int32_t*>(smem + kWaves * HC * lds_row_floats(D));
+    int32_t* tbl = reinterpret_cast<int32_t*>(red + kWaves * HC * lds_row_floats(D));
 
     // grid (Hkv, B, P): the partition index varies slowest (see the launcher)
     const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
@@ -221,7 +230,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const char* kc = static_cast<const char*>(p.k_cache);
     const char* vc = static_cast<const char*>(p.v_cache);
     const int64_t head_off = (int64_t)g * p.head_stride;               // elements
-    const uint32_t k_lane = (uint32_t)(16 * q4);                        // bytes
     const uint32_t v_lane = (uint32_t)(VE * c16 * EB);                  // bytes
     const int ntiles = (t1 - t0 + TT - 1) / TT;
 
@@ -240,16 +248,32 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const bool valid = jj < ntiles;
         const int tile_base = tile_start(jj);
         int phys = tb.phys, slot0 = tb.slot0, dt;
-        if constexpr (ALIGNED) {
-            dt = tile_row(tile_base, rg.lo, t1, mfma_k_offset(lane));
+        if constexpr (KWR) {
+            // whole rows: load s gives the lane 16 bytes of token mfma_k_token
+#pragma unroll
+            for (int s = 0; s < KL; ++s) {
+                const int tok = mfma_k_token(lane, s, LPT);
+                if constexpr (ALIGNED) {
+                    dt = tile_row(tile_base, rg.lo, t1, tok);
+                } else {
+                    locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, tok, phys, slot0, dt);
+                }
+                const int64_t base =
+                    EB * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
+                const uint32_t off = (uint32_t)dt * RB + 16 * (lane % LPT);
+                kr[s] = kBuf ? load_row16_buf(kc + base, off, valid) : load_row16(kc + base + off);
+            }
         } else {
-            locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, mfma_k_offset(lane), phys, slot0,
-                              dt);
-        }
-        {
+            // the operand layout: token l%16, bytes 64s + 16(l/16) for load s
+            if constexpr (ALIGNED) {
+                dt = tile_row(tile_base, rg.lo, t1, mfma_k_offset(lane));
+            } else {
+                locate_row<false>(p, tv, tlb0, tile_base, rg.lo, t1, mfma_k_offset(lane), phys,
+                                  slot0, dt);
+            }
             const int64_t base =
                 EB * ((int64_t)phys * p.block_stride + head_off + (int64_t)slot0 * D);
-            const uint32_t off = (uint32_t)dt * (EB * D) + k_lane;
+            const uint32_t off = (uint32_t)dt * RB + 16 * q4;
 #pragma unroll
             for (int s = 0; s < KL; ++s)
                 kr[s] = kBuf ? load_row16_buf(kc + base, off + 64 * s, valid)
@@ -294,15 +318,34 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     auto process = [&](int j, const uint4 (&kr)[KL], const VRaw (&vr)[4][DH]) {
         const int tile_base = t0 + j * TT;
         const bool full = full_tile(rg, tile_base, TT, t1);
+        // the whole-row K loads through the wave's LDS buffer into the operand
+        // layout (the wave's LDS operations complete in order, so each read
+        // sees this tile's writes, and the next tile's writes follow these
+        // reads); rows KSB apart keep both the writes and the reads free of
+        // bank conflicts
+        uint4 kx[KL];
+        if constexpr (KWR) {
+            char* kb = kst + wave * 16 * KSB;
+#pragma unroll
+            for (int s = 0; s < KL; ++s)
+                *reinterpret_cast<uint4*>(kb + mfma_k_token(lane, s, LPT) * KSB +
+                                          16 * (lane % LPT)) = kr[s];
+#pragma unroll
+            for (int s = 0; s < KL; ++s)
+                kx[s] = *reinterpret_cast<const uint4*>(kb + c16 * KSB + 64 * s + 16 * q4);
+        } else {
+#pragma unroll
+            for (int s = 0; s < KL; ++s) kx[s] = kr[s];
+        }
         // the A operands of the k-steps (fp8 bytes decoded to the 16-bit type)
         uint4 ka[KS];
 #pragma unroll
         for (int s = 0; s < KL; ++s) {
             if constexpr (F8) {
-                ka[2 * s] = fp8x8_to_16bit<Elt>(kr[s].x, kr[s].y);
-                ka[2 * s + 1] = fp8x8_to_16bit<Elt>(kr[s].z, kr[s].w);
+                ka[2 * s] = fp8x8_to_16bit<Elt>(kx[s].x, kx[s].y);
+                ka[2 * s + 1] = fp8x8_to_16bit<Elt>(kx[s].z, kx[s].w);
             } else {
-                ka[s] = kr[s];
+                ka[s] = kx[s];
             }
         }
         float sc[RC][4];
@@ -503,7 +546,7 @@ constexpr int kHead = PDA_HEAD;
 
 constexpr bool kF8 = PDA_KV_FP8 != 0;
 
-template <bool ALIGNED, bool BUF, int RC>
+template <bool ALIGNED, bool BUF, int RC, bool KWR>
 static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     // Workgroups are dispatched in grid order, partition by partition: the
@@ -511,23 +554,35 @@ static hipError_t launch_one(const DecodeParams& p, int batch, hipStream_t strea
     // every sequence instead of between them, where each one measured to cost
     // tens of ns of the whole launch (mixed lengths at batch 64: 16% faster).
     const dim3 grid(p.num_kv_heads, batch, p.num_partitions);
-    const size_t own = mfma_lds_bytes(kHead, p.tbl_capacity);
+    const size_t own = mfma_lds_bytes(kHead, kF8 ? 1 : 2, KWR, p.tbl_capacity);
     const uint32_t lds = (uint32_t)(own > (size_t)p.lds_floor ? own : (size_t)p.lds_floor);
     if (start || stop)
-        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8>), grid,
+        hipExtLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8, KWR>), grid,
                               dim3(kThreads), lds, stream, start, stop, 0, p);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8>), grid,
+        hipLaunchKernelGGL((decode_mfma_kernel<EltT, kHead, ALIGNED, BUF, RC, kF8, KWR>), grid,
                            dim3(kThreads), lds, stream, p);
     return hipGetLastError();
+}
+
+// Whole-row K loads where they measured faster (mfma_k_whole_rows); the
+// direct operand-layout loads are compiled only where they can be chosen.
+template <bool ALIGNED, bool BUF, int RC>
+static hipError_t launch_kwr(const DecodeParams& p, int batch, hipStream_t stream,
+                             hipEvent_t start, hipEvent_t stop) {
+    if constexpr (kHead == 128 && !kF8) {
+        if (!mfma_k_whole_rows(kHead, 2, p.tokens_per_part))
+            return launch_one<ALIGNED, BUF, RC, false>(p, batch, stream, start, stop);
+    }
+    return launch_one<ALIGNED, BUF, RC, true>(p, batch, stream, start, stop);
 }
 
 // One 16-row chunk for up to 16 rows per unit, two beyond.
 template <bool ALIGNED, bool BUF>
 static hipError_t launch_pv(const DecodeParams& p, int batch, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-    if (p.rows <= 16) return launch_one<ALIGNED, BUF, 1>(p, batch, stream, start, stop);
-    return launch_one<ALIGNED, BUF, 2>(p, batch, stream, start, stop);
+    if (p.rows <= 16) return launch_kwr<ALIGNED, BUF, 1>(p, batch, stream, start, stop);
+    return launch_kwr<ALIGNED, BUF, 2>(p, batch, stream, start, stop);
 }
 
 #define PDA_CAT2(a, b, c) a##_##b##_##c

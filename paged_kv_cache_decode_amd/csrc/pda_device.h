@@ -513,7 +513,7 @@ __device__ inline void locate_token(const DecodeParams& p, const int32_t* tbl, i
 
 // ---- MFMA tile geometry --------------------------------------------------
 // A 16-token tile.  K rows feed the A operand of v_mfma_f32_16x16x32 (S^T =
-// K Q^T): lane l reads token l%16, elements 32s + 8(l/16) .. +8 for k-step s.
+// K Q^T): lane l holds token l%16, elements 32s + 8(l/16) .. +8 for k-step s.
 // V rows feed the A operand of v_mfma_f32_16x16x16 (O^T = V^T P^T): for
 // round r lane l reads token 4(l/16) + r, elements dh*128 + VE*(l%16) .. +VE,
 // VE = 8 (16 lanes cover a 128-wide half dh) or 4 at D 64 (16 lanes cover
@@ -524,6 +524,14 @@ struct MfmaGeom {
     static constexpr int DH = D >= 128 ? D / 128 : 1; // 128-wide halves of V
     static constexpr int VE = D >= 128 ? 8 : 4;       // V elements per lane and round
 };
+// K rows are loaded whole: a row of RB bytes spans LPT = RB/16 lanes, so load
+// s of a tile gives lane l bytes 16*(l % LPT) .. +16 of token s*(64/LPT) +
+// l/LPT (every instruction reads whole 128-byte lines).  The tile then moves
+// through a per-wave LDS buffer of 16 rows, RB + 16 bytes apart, into the
+// A-operand layout above (lane l: token l%16, bytes 64s + 16(l/16) .. +16).
+__device__ inline int mfma_k_token(int lane, int s, int lpt) { return s * (64 / lpt) + lane / lpt; }
+// The token a lane loads when K is loaded in the operand layout directly
+// (mfma_k_whole_rows false): token l%16, bytes 64s + 16(l/16) for load s.
 __device__ inline int mfma_k_offset(int lane) { return lane & 15; }
 __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + r; }
 

@@ -97,7 +97,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int32_t> g_cu_count[kMaxDevices];
-constexpr int64_t kMaxLdsBytes = 64 * 1024;
+constexpr int64_t kMaxLdsBytes = 160 * 1024;  // a gfx950 workgroup may take all of a CU's LDS
 constexpr int32_t kMaxSeqLen = 1 << 30;
 constexpr int32_t kMaxGridYZ = 65535;
 // LDS of one decode workgroup when the launch spans several rounds: with
@@ -162,7 +162,10 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
                                                       (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else if (pl->variant == PDA_VARIANT_MFMA) {
-        const int64_t lds = (int64_t)mfma_lds_bytes(s->head_size, (int)table_capacity(s, pl));
+        const int eb = kv_fp8(s) ? 1 : 2;
+        const int64_t lds = (int64_t)mfma_lds_bytes(
+            s->head_size, eb, mfma_k_whole_rows(s->head_size, eb, pl->tokens_per_partition),
+            (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else {
         return PDA_ERR_INVALID;
@@ -436,7 +439,7 @@ int paged_decode_attn_trace(const pda_shape_t* s, const pda_plan_t* pl, int32_t 
     p.trace_part = trace_part;
     p.trace_range = trace_range;
     const bool aligned = block_aligned(s);
-    hipError_t e = launch_trace(s->head_size, aligned, pattern, p, s->num_seqs,
+    hipError_t e = launch_trace(s->head_size, kv_fp8(s) ? 1 : 2, aligned, pattern, p, s->num_seqs,
                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
 }

@@ -8,14 +8,15 @@
 // first_tile_blocks) -- but each lane that would load a token row records
 // which physical slot and which partition it used, instead of loading it.
 // ROWS selects whose rows: 0 the VALU kernel's (K and V alike), 1 the MFMA
-// kernel's K rows, 2 its V rows.  Tests compare the
+// kernel's K rows (whole-row loads of KB-byte elements), 2 its V rows.  Tests
+// compare the
 // trace bit for bit with a recomputation from the definition of the paged
 // cache.
 #include "pda_device.h"
 
 namespace pda {
 
-template <int D, bool ALIGNED, int ROWS>
+template <int D, int KB, bool ALIGNED, int ROWS>
 __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     using Geo = ValuGeom<D>;
     constexpr int LPT = Geo::LPT, R = Geo::R, U = Geo::U;
@@ -82,10 +83,21 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
                 if (c == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
         } else if constexpr (ROWS == 1) {
-            const int o = mfma_k_offset(lane);
-            locate(j, tile_base, o, phys, slot0, dt);
-            const int t = tile_base + o;
-            if ((lane >> 4) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
+            if (mfma_k_whole_rows(D, KB, p.tokens_per_part)) {
+                constexpr int LPT = KB * D / 16, KL = 16 / (64 / LPT);
+#pragma unroll
+                for (int s = 0; s < KL; ++s) {
+                    const int o = mfma_k_token(lane, s, LPT);
+                    locate(j, tile_base, o, phys, slot0, dt);
+                    const int t = tile_base + o;
+                    if (lane % LPT == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
+                }
+            } else {
+                const int o = mfma_k_offset(lane);
+                locate(j, tile_base, o, phys, slot0, dt);
+                const int t = tile_base + o;
+                if ((lane >> 4) == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
+            }
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -98,39 +110,46 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
     }
 }
 
-template <int D, bool ALIGNED, int ROWS>
+template <int D, int KB, bool ALIGNED, int ROWS>
 static hipError_t launch_trace_t(const DecodeParams& p, int batch, hipStream_t stream) {
     // Workgroups are dispatched in grid order, partition by partition: the
     // empty partitions of shorter sequences come after the live partitions of
     // every sequence instead of between them, where each one measured to cost
     // tens of ns of the whole launch (mixed lengths at batch 64: 16% faster).
     const dim3 grid(p.num_kv_heads, batch, p.num_partitions);
-    hipLaunchKernelGGL((trace_kernel<D, ALIGNED, ROWS>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((trace_kernel<D, KB, ALIGNED, ROWS>), grid, dim3(kThreads),
                        (size_t)p.tbl_capacity * sizeof(int32_t), stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int KB>
 static hipError_t launch_trace_d(bool aligned, int rows, const DecodeParams& p, int batch,
                                  hipStream_t s) {
     if (aligned) {
-        if (rows == 0) return launch_trace_t<D, true, 0>(p, batch, s);
-        if (rows == 1) return launch_trace_t<D, true, 1>(p, batch, s);
-        return launch_trace_t<D, true, 2>(p, batch, s);
+        if (rows == 0) return launch_trace_t<D, KB, true, 0>(p, batch, s);
+        if (rows == 1) return launch_trace_t<D, KB, true, 1>(p, batch, s);
+        return launch_trace_t<D, KB, true, 2>(p, batch, s);
     }
-    if (rows == 0) return launch_trace_t<D, false, 0>(p, batch, s);
-    if (rows == 1) return launch_trace_t<D, false, 1>(p, batch, s);
-    return launch_trace_t<D, false, 2>(p, batch, s);
+    if (rows == 0) return launch_trace_t<D, KB, false, 0>(p, batch, s);
+    if (rows == 1) return launch_trace_t<D, KB, false, 1>(p, batch, s);
+    return launch_trace_t<D, KB, false, 2>(p, batch, s);
 }
 
-hipError_t launch_trace(int head_size, bool aligned, int rows, const DecodeParams& p, int batch,
-                        hipStream_t stream) {
+template <int KB>
+static hipError_t launch_trace_kb(int head_size, bool aligned, int rows, const DecodeParams& p,
+                                  int batch, hipStream_t stream) {
     switch (head_size) {
-        case 64: return launch_trace_d<64>(aligned, rows, p, batch, stream);
-        case 128: return launch_trace_d<128>(aligned, rows, p, batch, stream);
-        case 256: return launch_trace_d<256>(aligned, rows, p, batch, stream);
+        case 64: return launch_trace_d<64, KB>(aligned, rows, p, batch, stream);
+        case 128: return launch_trace_d<128, KB>(aligned, rows, p, batch, stream);
+        case 256: return launch_trace_d<256, KB>(aligned, rows, p, batch, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_trace(int head_size, int kv_elt_bytes, bool aligned, int rows,
+                        const DecodeParams& p, int batch, hipStream_t stream) {
+    return kv_elt_bytes == 1 ? launch_trace_kb<1>(head_size, aligned, rows, p, batch, stream)
+                             : launch_trace_kb<2>(head_size, aligned, rows, p, batch, stream);
 }
 
 }  // namespace pda

@@ -133,7 +133,7 @@ hipError_t launch_zero_fill(void* dst, int64_t bytes, hipStream_t) {
     return hipSuccess;
 }
 
-hipError_t launch_trace(int, bool, int, const DecodeParams& p, int batch, hipStream_t) {
+hipError_t launch_trace(int, int, bool, int, const DecodeParams& p, int batch, hipStream_t) {
     // trace_range [B][Hkv][P][2]
     for (int b = 0; b < batch; ++b)
         for (int g = 0; g < p.num_kv_heads; ++g)
