@@ -15,8 +15,6 @@ so the rule is this library's own; what the pages fix is the reason for it:
 TP_ALIGN = 64
 VALU_MAX_GROUP = 8
 MFMA_MIN_GROUP = 2
-VALU_PLAN_ROWS = 4
-MFMA_MAX_UNITS = 128
 WG_MIN_BYTES = 64 * 1024
 WG_MANY_BYTES = 1024 * 1024
 WG_ONE_BYTES = 1024 * 1024
@@ -34,11 +32,10 @@ def _cdiv(a: int, b: int) -> int:
 
 def variant(num_seqs: int, num_kv_heads: int, group: int, q_len: int = 1,
             kv_fp8: bool = False) -> int:
-    """MFMA for fp8 KV, above 4 rows per unit, or for R = q_len * G >= 2
-    rows with at most 128 units."""
-    units = num_seqs * num_kv_heads
+    """MFMA for fp8 KV or for R = q_len * G >= 2 rows per unit; VALU for
+    one row."""
     rows = max(1, q_len) * group
-    if kv_fp8 or rows > VALU_PLAN_ROWS or (rows >= MFMA_MIN_GROUP and units <= MFMA_MAX_UNITS):
+    if kv_fp8 or rows >= MFMA_MIN_GROUP:
         return MFMA
     return VALU
 

@@ -142,13 +142,15 @@ __host__ __device__ constexpr int mfma_row_chunk(int head_size) {
 // Whether the MFMA kernel loads K in whole rows and moves each tile through
 // an LDS buffer into the matrix-core operand layout (otherwise it loads the
 // operand layout directly: 64 bytes of each of 16 rows per instruction).  By
-// measurement: whole rows at head sizes 64 and 256, for fp8 KV, and for
+// measurement: whole rows at head sizes 64 and 256, for fp8 KV, for
 // partitions of at most 512 tokens (a call's first loads are then a large
-// part of it); the direct loads for 16-bit KV at head size 128 with longer
-// partitions, where the LDS round trip measured 0.25 us slower per call.
+// part of it) and over more than 128 units (B * Hkv; many rounds of
+// workgroups); the direct loads for 16-bit KV at head size 128 with longer
+// partitions over few units, where the LDS round trip measured 0.2-0.3 us
+// slower per call.
 __host__ __device__ inline bool mfma_k_whole_rows(int head_size, int kv_elt_bytes,
-                                                  int tokens_per_part) {
-    return head_size != 128 || kv_elt_bytes != 2 || tokens_per_part <= 512;
+                                                  int tokens_per_part, int64_t units) {
+    return head_size != 128 || kv_elt_bytes != 2 || tokens_per_part <= 512 || units > 128;
 }
 
 // Bytes of the MFMA kernel's per-wave LDS buffers through which a K tile

@@ -571,7 +571,7 @@ template <bool ALIGNED, bool BUF, int RC>
 static hipError_t launch_kwr(const DecodeParams& p, int batch, hipStream_t stream,
                              hipEvent_t start, hipEvent_t stop) {
     if constexpr (kHead == 128 && !kF8) {
-        if (!mfma_k_whole_rows(kHead, 2, p.tokens_per_part))
+        if (!mfma_k_whole_rows(kHead, 2, p.tokens_per_part, (int64_t)p.num_kv_heads * batch))
             return launch_one<ALIGNED, BUF, RC, false>(p, batch, stream, start, stop);
     }
     return launch_one<ALIGNED, BUF, RC, true>(p, batch, stream, start, stop);

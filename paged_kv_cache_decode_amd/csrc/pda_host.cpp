@@ -164,7 +164,9 @@ int check_plan(const pda_shape_t* s, const pda_plan_t* pl) {
     } else if (pl->variant == PDA_VARIANT_MFMA) {
         const int eb = kv_fp8(s) ? 1 : 2;
         const int64_t lds = (int64_t)mfma_lds_bytes(
-            s->head_size, eb, mfma_k_whole_rows(s->head_size, eb, pl->tokens_per_partition),
+            s->head_size, eb,
+            mfma_k_whole_rows(s->head_size, eb, pl->tokens_per_partition,
+                              (int64_t)s->num_seqs * s->num_kv_heads),
             (int)table_capacity(s, pl));
         if (lds > kMaxLdsBytes) return PDA_ERR_UNSUPPORTED;
     } else {
@@ -309,8 +311,7 @@ int pda_plan_for_cus(const pda_shape_t* s, int32_t cu_count, pda_plan_t* plan) {
     // the rule documented in pda.h
     const int64_t R = rows_of(s);
     const int64_t units = (int64_t)s->num_seqs * s->num_kv_heads;
-    const bool mfma = kv_fp8(s) || R > PDA_VALU_PLAN_ROWS ||
-                      (R >= PDA_MFMA_MIN_GROUP && units <= PDA_MFMA_MAX_UNITS);
+    const bool mfma = kv_fp8(s) || R >= PDA_MFMA_MIN_GROUP;
     const int64_t bpt = (kv_fp8(s) ? 2 : 4) * (int64_t)s->head_size;
     const int64_t align = PDA_TP_ALIGN;
     const int64_t t_min = std::max(align, (PDA_WG_MIN_BYTES / bpt / align) * align);

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void trace_kernel(DecodeParams p) {
                 if (c == 0 && t >= rg.lo && t < t1) record(t, phys, slot0 + dt);
             }
         } else if constexpr (ROWS == 1) {
-            if (mfma_k_whole_rows(D, KB, p.tokens_per_part)) {
+            if (mfma_k_whole_rows(D, KB, p.tokens_per_part, (int64_t)p.num_kv_heads * gridDim.y)) {
                 constexpr int LPT = KB * D / 16, KL = 16 / (64 / LPT);
 #pragma unroll
                 for (int s = 0; s < KL; ++s) {

@@ -99,15 +99,18 @@ def test_cfg4_low_parallelism(L):
 
 
 # ---- config 5: batched mixed lengths ------------------------------------
-def test_cfg5_mixed_batch_full_size():
+@pytest.mark.parametrize("variant", [None, "valu"])
+def test_cfg5_mixed_batch_full_size(variant):
     """All 64 sequences (1.2M tokens, NaN tails) scored against the oracle,
     each at the tolerance, and the poisoned run bit-identical to the same
-    content with zero tails."""
+    content with zero tails; under the device's plan (the matrix cores) and
+    with the VALU kernel on the same partitions."""
     case = configs.cfg5(device="cuda")
-    got = run(case)
+    plan = None if variant is None else device_plan(case, variant=variant)
+    got = run(case, plan)
     check(case, got, per_seq=True)
     clean = kvgen.page(case, "zero", "zero")
-    assert np.array_equal(bits(got), bits(run(clean)))
+    assert np.array_equal(bits(got), bits(run(clean, plan)))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
