@@ -250,6 +250,18 @@ int64_t pda_workspace_bytes(const pda_shape_t* shape, const pda_plan_t* plan);
  * also be captured into a HIP graph. */
 int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* stream);
 
+/* Check a workspace's arrival counters (validation, not for the hot path):
+ * waits for the work queued on `stream`, copies the counter block (the first
+ * min(bytes, 4 * PDA_FUSED_MAX_UNITS) bytes) to the host and stores in
+ * *nonzero the number of counters that are not zero.  Once the calls that
+ * used the workspace have completed, every counter is zero; a non-zero count
+ * means a fused call started on counters that were not (a workspace not
+ * zeroed before its first use, or calls overlapping on one workspace), and
+ * that call's merge may not have run.  PDA_ERR_INVALID for a null pointer or
+ * a negative size, PDA_ERR_LAUNCH if the copy fails. */
+int paged_decode_attn_workspace_check(const void* workspace, int64_t bytes, void* stream,
+                                      int32_t* nonzero);
+
 /* The decode step, under the device's own plan.
  *   q            [B][q_len][Hq][D]    16-bit, the query rows of each sequence
  *   k_cache      [NB][Hkv][bs][D]     16-bit or fp8 (kv_dtype), the paged K pool

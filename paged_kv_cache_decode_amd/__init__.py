@@ -99,6 +99,9 @@ def load_library():
     lib.paged_decode_attn_trace.restype = ctypes.c_int
     lib.paged_decode_attn_workspace_init.argtypes = [P, ctypes.c_int64, P]
     lib.paged_decode_attn_workspace_init.restype = ctypes.c_int
+    lib.paged_decode_attn_workspace_check.argtypes = [P, ctypes.c_int64, P,
+                                                      ctypes.POINTER(ctypes.c_int32)]
+    lib.paged_decode_attn_workspace_check.restype = ctypes.c_int
     lib.paged_decode_attn_noalloc.argtypes = [sp, P, P, P, P, P, ctypes.c_float, P, P]
     lib.paged_decode_attn_noalloc.restype = ctypes.c_int
     lib.pda_status_string.argtypes = [ctypes.c_int]
@@ -313,6 +316,19 @@ def paged_decode_attn_workspace_init(workspace, stream=None):
     rc = load_library().paged_decode_attn_workspace_init(_ptr(workspace), nbytes, _stream(stream))
     if rc != PDA_OK:
         raise PdaError(rc, "paged_decode_attn_workspace_init")
+
+
+def paged_decode_attn_workspace_check(workspace, stream=None) -> int:
+    """Number of non-zero arrival counters in a workspace, after the work on
+    the stream (0 unless a fused call started on counters that were not
+    zero).  Synchronises the stream: a validation aid, not for the hot path."""
+    nbytes = workspace.numel() * workspace.element_size()
+    n = ctypes.c_int32(0)
+    rc = load_library().paged_decode_attn_workspace_check(_ptr(workspace), nbytes,
+                                                          _stream(stream), ctypes.byref(n))
+    if rc != PDA_OK:
+        raise PdaError(rc, "paged_decode_attn_workspace_check")
+    return int(n.value)
 
 
 def pda_read_probe(src, sink, workgroups: int = 2048, stream=None):

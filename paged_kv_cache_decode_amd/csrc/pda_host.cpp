@@ -4,6 +4,7 @@
 #include <atomic>
 #include <math.h>
 #include <stdint.h>
+#include <vector>
 
 #include "pda_common.h"
 
@@ -361,6 +362,24 @@ int paged_decode_attn_workspace_init(void* workspace, int64_t bytes, void* strea
     // a fill kernel, not a memset: a caller may capture this into a HIP graph
     hipError_t e = launch_zero_fill(workspace, bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PDA_OK : PDA_ERR_LAUNCH;
+}
+
+int paged_decode_attn_workspace_check(const void* workspace, int64_t bytes, void* stream,
+                                      int32_t* nonzero) {
+    if (!nonzero || bytes < 0 || (bytes > 0 && !workspace)) return PDA_ERR_INVALID;
+    *nonzero = 0;
+    const int64_t n = std::min<int64_t>(bytes, kCounterBytes) / 4;
+    if (n == 0) return PDA_OK;
+    std::vector<int32_t> host((size_t)n);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(host.data(), workspace, (size_t)n * 4, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return PDA_ERR_LAUNCH;
+    int32_t count = 0;
+    for (int32_t v : host) count += v != 0;
+    *nonzero = count;
+    return PDA_OK;
 }
 
 int paged_decode_attn_plan(const pda_shape_t* s, pda_plan_t* plan) {

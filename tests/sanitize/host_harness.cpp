@@ -34,6 +34,13 @@ extern "C" hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, in
     *value = g_cu_count;
     return hipSuccess;
 }
+// "device" buffers are host memory here
+extern "C" hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind,
+                                     hipStream_t) {
+    memcpy(dst, src, bytes);
+    return hipSuccess;
+}
+extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 
 namespace pda {
 
@@ -267,6 +274,25 @@ int main(int argc, char** argv) {
                 EXPECT(rc == PDA_OK || (merge == PDA_MERGE_FUSED && rc == PDA_ERR_UNSUPPORTED));
             }
         }
+    }
+    // the workspace check counts the counters left non-zero, within the
+    // counter block and the buffer's own size only
+    {
+        std::vector<int32_t> ws(16384 + 64, 0);
+        int32_t nz = -1;
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), (int64_t)ws.size() * 4, nullptr, &nz) ==
+               PDA_OK && nz == 0);
+        ws[7] = 3;
+        ws[16383] = -1;
+        ws[16384] = 5;  // past the counter block: partial data, not counted
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), (int64_t)ws.size() * 4, nullptr, &nz) ==
+               PDA_OK && nz == 2);
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), 28, nullptr, &nz) == PDA_OK && nz == 0);
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), 32, nullptr, &nz) == PDA_OK && nz == 1);
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), -4, nullptr, &nz) == PDA_ERR_INVALID);
+        EXPECT(paged_decode_attn_workspace_check(nullptr, 4, nullptr, &nz) == PDA_ERR_INVALID);
+        EXPECT(paged_decode_attn_workspace_check(ws.data(), 4, nullptr, nullptr) == PDA_ERR_INVALID);
+        EXPECT(paged_decode_attn_workspace_check(nullptr, 0, nullptr, &nz) == PDA_OK && nz == 0);
     }
     // 2. random valid shapes under their plan, and under random forced plans
     int forced_ok = 0;

@@ -245,6 +245,34 @@ def test_fused_merge_across_xcds_repeated(dtype):
     assert int(ws[:16384 * 4].view(torch.int32).abs().sum().item()) == 0
 
 
+def test_workspace_check_reports_stale_counters():
+    """The arrival counters are all zero after fused calls; a counter left
+    non-zero before a fused call (as in a workspace never zeroed) is reported
+    by paged_decode_attn_workspace_check, and zeroing the workspace clears
+    it.  (The planted value only keeps that unit's last workgroup from
+    merging; every kernel still ends normally.)"""
+    case = configs.cfg2(32, 2048, device="cuda")
+    shape = shape_of(case)
+    plan = pda.paged_decode_attn_plan(shape)
+    plan.merge = pda.PDA_MERGE_FUSED
+    assert plan.num_partitions > 1
+    ws = torch.zeros(pda.pda_workspace_bytes(shape, plan), dtype=torch.uint8, device="cuda")
+
+    def call():
+        return pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table,
+                                     case.seq_lens_t, case.scale, workspace=ws,
+                                     max_seq_len=case.max_seq_len, plan=plan)
+    check(case, call())
+    assert pda.paged_decode_attn_workspace_check(ws) == 0
+    ws[:4].view(torch.int32)[0] = plan.num_partitions + 3  # unit (0, 0)
+    call()
+    assert pda.paged_decode_attn_workspace_check(ws) == 1
+    pda.paged_decode_attn_workspace_init(ws)
+    assert pda.paged_decode_attn_workspace_check(ws) == 0
+    check(case, call())
+    assert pda.paged_decode_attn_workspace_check(ws) == 0
+
+
 def test_one_workspace_serves_a_sequence_of_shapes():
     """Zeroed once, one workspace serves calls of different shapes under the
     device plan, fused merge and merge kernel alike: the arrival counters sit
