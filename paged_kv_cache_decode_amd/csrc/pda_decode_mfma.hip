@@ -145,7 +145,8 @@ struct VChunk<4> {
 // The unit's R = q_len * G rows (row r: query position r / G, head r % G)
 // are packed in RC chunks of 16 (RC = 2 for R > 16): each K tile feeds RC
 // QK and RC PV products, and each chunk keeps its own softmax state and
-// accumulators.
+// accumulators.  KWR: K is loaded in whole rows and moved into the operand
+// layout through the wave's LDS buffer (mfma_k_whole_rows picks it per call).
 template <typename Elt, int D, bool ALIGNED, bool BUF, int RC, bool F8, bool KWR>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     static_assert(RC == 1 || RC == 2, "one or two 16-row chunks");
