@@ -399,6 +399,31 @@ def test_bookkeeping_trace_bit_exact(D, bs, G, lens, forced, variant, rows):
     assert np.array_equal(ranges, e_ranges)
 
 
+@pytest.mark.parametrize("rows", [0, 1])
+@pytest.mark.parametrize("D,bs,G,lens,forced", TRACE_CASES)
+def test_bookkeeping_trace_fp8_kv(D, bs, G, lens, forced, rows):
+    """The matrix-core kernel's K and V rows for fp8 KV, whose whole-row K
+    loads have their own lane map (a row is D bytes, not 2D)."""
+    Hkv = 2
+    case = to_device(kvgen.make_case(len(lens), G * Hkv, Hkv, D, bs, lens, seed=102,
+                                     extra_blocks=3, kv_dtype="fp8"))
+    shape = shape_of(case)
+    plan = pda.paged_decode_attn_plan(shape) if forced is None else plan_of(*forced)
+    plan.variant = pda.PDA_VARIANT_MFMA
+    slot, part, ranges = pda.paged_decode_attn_trace(shape, plan, case.block_table,
+                                                     case.seq_lens_t, rows=rows)
+    torch.cuda.synchronize()
+    e_slot, e_part, e_ranges, valid = bookkeeping.expected_trace(
+        case.block_table.cpu().numpy(), case.seq_lens, Hkv, bs, case.max_seq_len,
+        plan.num_partitions, plan.tokens_per_partition)
+    slot, part, ranges = slot.cpu().numpy(), part.cpu().numpy(), ranges.cpu().numpy()
+    Lm = case.max_seq_len
+    assert np.array_equal(slot[..., :Lm][valid], e_slot[valid])
+    assert np.array_equal(part[..., :Lm][valid], e_part[valid])
+    assert np.all(slot[..., :Lm][~valid] == -1) and np.all(part[..., :Lm][~valid] == -1)
+    assert np.array_equal(ranges, e_ranges)
+
+
 @pytest.mark.parametrize("variant,rows", [("valu", 0), ("mfma", 0), ("mfma", 1)])
 def test_bookkeeping_trace_cfg5_full_size(variant, rows):
     case = configs.cfg5(device="cuda")
