@@ -529,10 +529,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
             }
         }
         __syncthreads();
-        // the combine takes kHeadChunk rows per pass (one row per 32 threads)
-        for (int r0 = 0; r0 < hn; r0 += kHeadChunk)
-            write_unit_rows<Elt, D, true>(p, red + r0 * lds_row_floats(D), HC, h0 + r0, min(kHeadChunk, hn - r0), b,
-                                    g, part);
+        // the combine: up to 8 rows in one pass of 32 threads per row, 9 to
+        // 16 rows in one pass of 16 threads per row
+        bool done = false;
+        if constexpr (HC > kHeadChunk) {
+            if (hn > kHeadChunk) {
+                write_unit_rows<Elt, D, true, 16>(p, red, HC, h0, hn, b, g, part);
+                done = true;
+            }
+        }
+        if (!done) write_unit_rows<Elt, D, true>(p, red, HC, h0, hn, b, g, part);
         if (h0 + HC < R) __syncthreads();  // before the next chunk reuses red
     }
     if (!direct && p.fused_merge) fused_merge_tail<Elt, D>(p, rg, b, g);

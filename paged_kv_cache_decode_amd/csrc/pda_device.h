@@ -540,24 +540,24 @@ __device__ inline int mfma_v_offset(int lane, int r) { return 4 * (lane >> 4) + 
 // Combine the kWaves per-wave states of rows h0 .. h0+hn-1 of unit (b, g),
 // staged in LDS as red[w][i][0..D) = unnormalised O, red[w][i][D] = running
 // max m (exp2 domain), red[w][i][D+1] = denominator l (red_heads rows per
-// wave, hn <= min(red_heads, 8)), in a fixed order, and write either the
-// 16-bit output (one partition) or the fp32 partial.  32 threads per row (8
-// rows at a time); thread j of a row takes the element pairs d = 2j + 64k
-// (k < D/64), so a row's threads read 64 consecutive floats of LDS per pair
-// (8 consecutive elements per thread put threads 4 apart on the same banks)
-// and write 256 contiguous bytes of output or partials per pair and row.
+// wave, hn <= min(red_heads, kThreads / TPR)), in a fixed order, and write
+// either the 16-bit output (one partition) or the fp32 partial.  TPR threads
+// per row (32: 8 rows at a time; 16: 16 rows at a time); thread j of a row
+// takes the element pairs d = 2j + 2*TPR*k (k < D/(2*TPR)), so a row's
+// threads read 2*TPR consecutive floats of LDS per pair (8 consecutive
+// elements per thread put threads 4 apart on the same banks) and write
+// 8*TPR contiguous bytes of output or partials per pair and row.
 // All LDS reads of the step are issued before any arithmetic.  WT: partials
 // for the merge kernel are written through to the device coherence point
 // (device-scope stores), leaving no dirty L2 lines for the end of the launch
 // to write back (measured faster for the matrix-core kernel, slightly slower
 // for the VALU one).
-template <typename Elt, int D, bool WT>
+template <typename Elt, int D, bool WT, int TPR = 32>
 __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, int red_heads,
                                        int h0, int hn, int b, int g, int part) {
-    constexpr int kTpr = 32;        // threads per row
-    constexpr int KP = D / 64;      // element pairs per thread: 1, 2 or 4
-    static_assert(kThreads == 8 * kTpr, "rows of 32 threads");
-    const int i = threadIdx.x / kTpr, j = threadIdx.x % kTpr;
+    constexpr int KP = D / (2 * TPR);  // element pairs per thread
+    static_assert((TPR == 16 || TPR == 32) && KP >= 1 && kThreads % TPR == 0, "rows of threads");
+    const int i = threadIdx.x / TPR, j = threadIdx.x % TPR;
     if (i >= hn) return;
     // every LDS read of the step first: the waves' (m, l) and the row's pairs
     float mw[kWaves], lw[kWaves];
@@ -568,7 +568,8 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
         mw[w] = rw[D];
         lw[w] = rw[D + 1];
 #pragma unroll
-        for (int k = 0; k < KP; ++k) vw[w][k] = *reinterpret_cast<const float2*>(rw + 2 * j + 64 * k);
+        for (int k = 0; k < KP; ++k)
+            vw[w][k] = *reinterpret_cast<const float2*>(rw + 2 * j + 2 * TPR * k);
     }
     float M = -FLT_MAX;
 #pragma unroll
@@ -604,7 +605,7 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
         uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + row * D);
 #pragma unroll
         for (int k = 0; k < KP; ++k)
-            dst[j + 32 * k] = (uint32_t)Elt::from_float(o[k].x) |
+            dst[j + TPR * k] = (uint32_t)Elt::from_float(o[k].x) |
                               ((uint32_t)Elt::from_float(o[k].y) << 16);
         return;
     }
@@ -619,7 +620,7 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
 #pragma unroll
             for (int k = 0; k < KP; ++k) {
                 const float v2[2] = {o[k].x, o[k].y};
-                store_coherent_vec<2>(obase, off + 256 * k, v2);
+                store_coherent_vec<2>(obase, off + 8 * TPR * k, v2);
             }
             if (j == 0) {
                 const float mlv[2] = {M, den};
@@ -629,8 +630,8 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
             float* dst = p.ws_o + prow * D;
 #pragma unroll
             for (int k = 0; k < KP; ++k) {
-                store_coherent(dst + 2 * j + 64 * k, o[k].x);
-                store_coherent(dst + 2 * j + 64 * k + 1, o[k].y);
+                store_coherent(dst + 2 * j + 2 * TPR * k, o[k].x);
+                store_coherent(dst + 2 * j + 2 * TPR * k + 1, o[k].y);
             }
             if (j == 0) {
                 store_coherent(p.ws_ml + prow * 2, M);
@@ -640,7 +641,7 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
     } else {              // read by the merge kernel after this launch
         float2* dst = reinterpret_cast<float2*>(p.ws_o + prow * D);
 #pragma unroll
-        for (int k = 0; k < KP; ++k) dst[j + 32 * k] = o[k];
+        for (int k = 0; k < KP; ++k) dst[j + TPR * k] = o[k];
         if (j == 0) reinterpret_cast<float2*>(p.ws_ml)[prow] = make_float2(M, den);
     }
 }
