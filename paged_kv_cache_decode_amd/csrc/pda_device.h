@@ -557,6 +557,9 @@ __device__ inline void write_unit_rows(const DecodeParams& p, const float* red, 
                                        int h0, int hn, int b, int g, int part) {
     constexpr int KP = D / (2 * TPR);  // element pairs per thread
     static_assert((TPR == 16 || TPR == 32) && KP >= 1 && kThreads % TPR == 0, "rows of threads");
+    // one pass serves every row its callers stage: up to kHeadChunk rows at
+    // 32 threads per row, up to 16 at 16
+    static_assert(kThreads / TPR >= (TPR == 32 ? kHeadChunk : 16), "a thread row per staged row");
     const int i = threadIdx.x / TPR, j = threadIdx.x % TPR;
     if (i >= hn) return;
     // every LDS read of the step first: the waves' (m, l) and the row's pairs
