@@ -208,14 +208,28 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+_TENSOR_NAMES = ("q", "k_cache", "v_cache", "block_table", "seq_lens", "out")
+
+
 def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
     import torch
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
-                    ("block_table", block_table), ("seq_lens", seq_lens), ("out", out)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    ts = (q, k_cache, v_cache, block_table, seq_lens, out)
+    # the library launches on the current device: every buffer must be a
+    # contiguous tensor there (get_device() is -1 for a host tensor)
+    dev = q.get_device()
+    ok = dev >= 0
+    for t in ts:
+        ok = ok and t.get_device() == dev and t.is_contiguous()
+    if not ok or dev != torch.cuda.current_device():
+        for name, t in zip(_TENSOR_NAMES, ts):
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if any(t.get_device() != dev for t in ts):
+            raise ValueError("q, k_cache, v_cache, block_table, seq_lens and out must share one "
+                             "device")
+        raise ValueError("the tensors must be on the current device")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
     if q.dtype != out.dtype or k_cache.dtype != v_cache.dtype:
@@ -228,6 +242,29 @@ def _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out):
         raise ValueError("out must have the shape of q")
     if seq_lens.shape != (q.shape[0],) or block_table.shape[0] != q.shape[0]:
         raise ValueError("seq_lens / block_table do not match the batch")
+
+
+# The shape descriptor and the device plan's workspace size of recent calls,
+# by the tensors' geometry: a decode loop calls with the same geometry every
+# step, and building the descriptor and querying the plan cost more host
+# time than the rest of the binding.  The descriptors are private (passed by
+# reference to the library only, never handed out).
+_SHAPE_CACHE = {}
+_SHAPE_CACHE_MAX = 256
+
+
+def _shape_and_workspace(q, k_cache, block_table, max_seq_len, sliding_window, k_scale,
+                         v_scale):
+    key = (q.get_device(), q.shape, q.dtype, k_cache.shape, k_cache.dtype, block_table.shape[1],
+           max_seq_len, sliding_window, k_scale, v_scale)
+    hit = _SHAPE_CACHE.get(key)
+    if hit is None:
+        shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window, k_scale,
+                                   v_scale)
+        if len(_SHAPE_CACHE) >= _SHAPE_CACHE_MAX:
+            _SHAPE_CACHE.clear()
+        hit = _SHAPE_CACHE[key] = (shape, paged_decode_attn_workspace_size(shape))
+    return hit
 
 
 def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, out=None,
@@ -251,13 +288,14 @@ def paged_decode_attn(q, k_cache, v_cache, block_table, seq_lens, scale: float, 
     _check_tensors(q, k_cache, v_cache, block_table, seq_lens, out)
     if max_seq_len is None:
         max_seq_len = block_table.shape[1] * k_cache.shape[2]
-    shape = shape_from_tensors(q, k_cache, block_table, max_seq_len, sliding_window, k_scale,
-                               v_scale)
+    shape, need = _shape_and_workspace(q, k_cache, block_table, max_seq_len, sliding_window,
+                                       k_scale, v_scale)
     lib = load_library()
-    if plan is None:
-        need = paged_decode_attn_workspace_size(shape)
-    else:
+    if plan is not None:
         need = pda_workspace_bytes(shape, plan)
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous() or
+                                  workspace.get_device() != q.get_device()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # zeroed, as required
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

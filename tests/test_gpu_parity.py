@@ -316,6 +316,27 @@ def test_edge_lengths():
         check(case, got, per_seq=False)
 
 
+def test_binding_refuses_buffers_off_the_device():
+    """A workspace or a table on the host is refused before the library is
+    called: a host address handed to a kernel would be a GPU memory fault.
+    The device buffers of the same call then still decode it."""
+    case = to_device(configs.cfg1("bf16"))
+    plan = pda.paged_decode_attn_plan(shape_of(case))
+    plan.num_partitions, plan.tokens_per_partition = 2, 64  # P > 1: a workspace is used
+    plan.workspace_bytes = pda.pda_workspace_bytes(shape_of(case), plan)
+    args = (case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens_t, case.scale)
+    with pytest.raises(ValueError, match="workspace"):
+        pda.paged_decode_attn(*args, plan=plan,
+                              workspace=torch.zeros(plan.workspace_bytes, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device"):
+        pda.paged_decode_attn(case.q, case.k_cache, case.v_cache, case.block_table.cpu(),
+                              case.seq_lens_t, case.scale)
+    ws = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=case.q.device)
+    got = pda.paged_decode_attn(*args, plan=plan, workspace=ws)
+    torch.cuda.synchronize()
+    check(case, got)
+
+
 def test_empty_batch_rows_only():
     case = to_device(kvgen.make_case(2, 8, 4, 128, 16, [0, 0], seed=5, max_blocks_per_seq=2,
                                      max_seq_len=32))
