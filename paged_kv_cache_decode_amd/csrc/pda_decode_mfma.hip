@@ -153,8 +153,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     using Geo = MfmaGeom<D>;
     constexpr int KS = Geo::KS, DH = Geo::DH, VE = Geo::VE, TT = 16;
     constexpr int EB = F8 ? 1 : 2;             // KV bytes per element
-    // tiles in register buffers (fp8 tiles are half the bytes and registers)
-    constexpr int S = F8 ? PDA_MFMA_STAGES_FP8 : PDA_MFMA_STAGES;
+    // tiles in register buffers (fp8 tiles are half the bytes and registers);
+    // a wave's K+V tile under 4 KiB (fp8 at head size 64) takes four, which
+    // keep enough bytes in flight (two: 6 % slower per call)
+    constexpr int S = 2 * TT * D * EB < 4096 ? 4 : F8 ? PDA_MFMA_STAGES_FP8 : PDA_MFMA_STAGES;
     static_assert(S >= 2 && S <= 6, "stages");
     constexpr int KL = F8 ? KS / 2 : KS;       // 16-byte K loads per lane and tile
     using VC = VChunk<VE * EB>;
