@@ -316,6 +316,33 @@ def test_edge_lengths():
         check(case, got, per_seq=False)
 
 
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
+def test_units_at_the_counter_block_limit(variant):
+    """B * Hkv = PDA_FUSED_MAX_UNITS (16384) under the fused merge: every
+    arrival counter is in use, the last one included, over many rounds of
+    workgroups; parity on every sequence, and (in `run`) the counters back at
+    zero and the guard bytes intact."""
+    rng = np.random.default_rng(16384)
+    lens = [int(x) for x in rng.integers(17, 129, size=2048)]
+    case = to_device(kvgen.make_case(2048, 8, 8, 64, 16, lens, seed=16384, tail_k="nan",
+                                     tail_v="nan"))
+    assert case.B * case.Hkv == 16384
+    got = run(case, plan=plan_of(2, 64, variant=VARIANTS[variant], merge=pda.PDA_MERGE_FUSED))
+    check(case, got, per_seq=True)
+
+
+def test_block_larger_than_a_partition():
+    """Blocks of 4096 tokens, far larger than a partition: each partition
+    lies in one or two blocks.  Parity under the device plan and two forced
+    plans (the bookkeeping trace of the same shape is one of TRACE_CASES)."""
+    lens = [4096, 4097, 9000, 1]
+    case = to_device(kvgen.make_case(4, 16, 4, 128, 4096, lens, seed=4096, tail_k="nan",
+                                     tail_v="nan"))
+    for plan in (None, plan_of(3, 4096, variant=pda.PDA_VARIANT_MFMA),
+                 plan_of(16, 576, variant=pda.PDA_VARIANT_MFMA, merge=pda.PDA_MERGE_FUSED)):
+        check(case, run(case, plan=plan), per_seq=True)
+
+
 def test_binding_refuses_buffers_off_the_device():
     """A workspace or a table on the host is refused before the library is
     called: a host address handed to a kernel would be a GPU memory fault.
@@ -393,6 +420,7 @@ TRACE_CASES = [
     (64, 5, 3, [1234, 0, 99], (3, 512)),
     (128, 48, 8, [5000, 4999], None),
     (256, 8, 2, [777, 8], (2, 512)),
+    (128, 4096, 4, [4096, 4097, 9000, 1], (16, 576)),
 ]
 
 
