@@ -71,9 +71,14 @@ def plans_for(case, variant):
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("D,bs,G,lens,W", WINDOW_CASES)
 def test_window_parity(D, bs, G, lens, W, variant):
-    if variant == "valu" and G > 8:
-        pytest.skip("the VALU variant serves groups of up to 8 heads")
     case = window_case(D, bs, G, lens, W, seed=D * 7 + bs + G + W)
+    if variant == "valu" and G > 8:
+        # beyond the VALU variant's groups of 8: refused on the host
+        for plan in plans_for(case, variant):
+            with pytest.raises(pda.PdaError) as err:
+                run(case, plan=plan)
+            assert err.value.status == pda.PDA_ERR_UNSUPPORTED
+        return
     ref = reference(case)
     for plan in plans_for(case, variant):
         print(f"plan P={plan.num_partitions} T={plan.tokens_per_partition} "
@@ -124,10 +129,16 @@ def test_window_of_one_token_is_the_last_v_row(variant):
 @pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("D,bs,G,lens,W", WINDOW_CASES)
 def test_window_trace_bit_exact(D, bs, G, lens, W, variant, rows):
-    if variant == "valu" and G > 8:
-        pytest.skip("the VALU variant serves groups of up to 8 heads")
     case = window_case(D, bs, G, lens, W, seed=101)
     shape = shape_of(case)
+    if variant == "valu" and G > 8:
+        # beyond the VALU variant's groups of 8: the trace refuses its plans
+        for plan in plans_for(case, variant)[:3]:
+            with pytest.raises(pda.PdaError) as err:
+                pda.paged_decode_attn_trace(shape, plan, case.block_table, case.seq_lens_t,
+                                            rows=rows)
+            assert err.value.status == pda.PDA_ERR_UNSUPPORTED
+        return
     for plan in plans_for(case, variant)[:3]:
         slot, part, ranges = pda.paged_decode_attn_trace(shape, plan, case.block_table,
                                                          case.seq_lens_t, rows=rows)
