@@ -46,9 +46,9 @@ def test_traffic_summary_is_keyed_to_kernel_and_sources():
 
 
 def test_design_table_is_the_stored_bench_line():
-    """The results table in the design doc is printed from the stored bench line
-    (profiles/bench_full.json) by `bench.py --table`, not typed by hand: the
-    rendered table appears in the document verbatim."""
+    """The results table of the design document is printed from the stored
+    bench line (profiles/bench_full.json) by `bench.py --table`, not typed by
+    hand: the rendered table appears in the document verbatim."""
     r = _run(["--table", os.path.join(ROOT, "profiles", "bench_full.json")])
     assert r.returncode == 0, r.stderr
     table = r.stdout.strip()
