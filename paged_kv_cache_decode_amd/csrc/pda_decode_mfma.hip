@@ -8,10 +8,13 @@
 //
 //   QK^T  S^T = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: a 16-token tile of K
 //         rows is the A operand (lane l holds 16 bytes of token l%16 per
-//         k-step), Q^T the B operand.  K is loaded in whole rows (each load
+//         k-step), Q^T the B operand.  Where it measured faster
+//         (mfma_k_whole_rows) K is loaded in whole rows (each load
 //         instruction reads whole 128-byte lines, where the operand layout
-//         would read 64 bytes of each of 16 rows) and moved into the operand
-//         layout through the wave's own LDS buffer.  The 16x16 result leaves
+//         reads 64 bytes of each of 16 rows) and moved into the operand
+//         layout through the wave's own LDS buffer; elsewhere (16-bit KV at
+//         head size 128, long partitions, few units) it is loaded straight
+//         into the operand layout.  The 16x16 result leaves
 //         each lane the scores of one row (l%16) for four tokens (4(l/16) +
 //         r, r = 0..3).
 //   mask  scores of tokens at or past the partition end, outside a sliding
@@ -60,7 +63,8 @@
 #ifndef PDA_KV_FP8
 #define PDA_KV_FP8 0
 #endif
-// Register-buffer stages of the tile pipeline, chosen by measurement
+// Register-buffer stages of the tile pipeline, chosen by measurement (the
+// kernel takes four for K+V tiles under 4 KiB per wave, see below)
 #ifndef PDA_MFMA_STAGES
 #define PDA_MFMA_STAGES 2
 #endif
